@@ -1,0 +1,296 @@
+"""Decode-attention benchmark on one MI355X: decode µs/step and achieved HBM GB/s.
+
+One step = one full decode call (split kernel + merge kernel when the plan has
+more than one split) over one batch of synthetic input already resident in HBM.
+The KV cache is rotated over enough device copies that every step reads it cold
+(at least 512 MiB between reuses: twice the 256 MiB Infinity Cache).
+
+Printed: one JSON line with the metric, the whole-step throughput (unique K+V
+bytes / step time), the dominant kernel's roofline (its own launch durations
+timed with HIP events on the stream it runs on) and the float64 CPU oracle's
+throughput on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep] [--no-cpu-baseline]
+  python bench.py --copy-probe BYTES   # a plain device copy, to scale rocprof byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/step + achieved HBM GB/s (fraction of peak), KV 4k→128k"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+COLD_BYTES = 512 << 20      # bytes touched between reuses of one KV copy
+DEFAULT_WORKLOAD = "decode_bf16_h32_s4096"
+SPLIT_KERNEL = "split_valu_kernel"
+SWEEP = (4096, 8192, 16384, 32768, 65536, 131072, 131073)
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: a committed counter profile is used only while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_13_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str) -> dict | None:
+    """HBM bytes per split-kernel launch from the committed rocprofv3 --pmc summary."""
+    path = os.path.join(ROOT, "profiles", f"{SPLIT_KERNEL}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return t
+
+
+class Case:
+    """A workload placed in device memory with rotated KV copies and its C-ABI arguments."""
+
+    def __init__(self, w, chunk: int = 0):
+        import torch
+
+        import decode_attention_13_amd as fd
+        from decode_attention_13_amd import binding
+
+        self.w = w
+        self.fd = fd
+        self.lib = fd.lib()
+        dev = torch.device("cuda:0")
+        log(f"generating {w.name}")
+        d = w.make()
+        self.d = d
+        self.opt = fd.options(force_chunk=chunk) if chunk else None
+        esize = torch.tensor([], dtype=inputs_dtype(w.dtype)).element_size()
+        self.dtype_code = binding.FD_DTYPE[inputs_dtype(w.dtype)]
+        if w.kind == "single":
+            self.kv_bytes = 2 * w.S * w.Hkv * 128 * esize
+            self.units = w.S * w.Hkv
+            self.plan = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 0, self.opt)
+            self.q = d["q"].to(dev)
+            srcs = (d["k"], d["v"])
+        else:
+            self.total = d["total_kv"]
+            self.kv_bytes = 2 * self.total * w.Hkv * 128 * esize
+            self.units = self.total * w.Hkv
+            self.plan = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, d["max_seq_len"], self.total, 0, self.opt)
+            self.q = d["q"].to(dev)
+            self.table = d["block_table"].to(dev)
+            self.lens = d["seq_lens"].to(dev)
+            srcs = (d["k_cache"], d["v_cache"])
+        self.copies = max(1, math.ceil(COLD_BYTES / self.kv_bytes))
+        kd, vd = srcs[0].to(dev), srcs[1].to(dev)
+        self.kv = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(self.copies - 1)]
+        self.o = torch.empty_like(self.q)
+        self.ws = torch.empty(max(1, self.plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+        log(f"{w.name}: plan {self.plan}, {self.copies} KV copies of {self.kv_bytes / 1e6:.1f} MB")
+
+    def step(self, i: int, opt=None) -> None:
+        import ctypes
+        k, v = self.kv[i % self.copies]
+        o = opt if opt is not None else self.opt
+        optp = ctypes.byref(o) if o is not None else None
+        w = self.w
+        if w.kind == "single":
+            rc = self.lib.fd_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), w.H, w.Hkv, w.S,
+                                    128, self.dtype_code, self.d["scale"], self.ws.data_ptr(),
+                                    self.ws.numel(), optp, self.stream.cuda_stream)
+        else:
+            rc = self.lib.fd_paged_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.table.data_ptr(),
+                                          self.lens.data_ptr(), w.page_size, self.o.data_ptr(), self.d["scale"], w.B,
+                                          w.H, w.Hkv, 128, self.d["num_pages"], self.d["max_blocks"],
+                                          self.d["max_seq_len"], self.total, self.dtype_code, self.ws.data_ptr(),
+                                          self.ws.numel(), optp, self.stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"{self.lib.fd_status_string(rc).decode()}: {self.lib.fd_last_error().decode()}")
+
+
+def inputs_dtype(name: str):
+    from decode_attention_13_amd.inputs import DTYPES
+    return DTYPES[name]
+
+
+def time_steps(case: Case, steps: int, warmup: int) -> dict:
+    """Whole-step wall time over exactly `steps` steps, then the split kernel alone
+    (events on the launch stream around each split kernel) over another `steps`."""
+    import torch
+
+    for i in range(warmup):
+        case.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        case.step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+
+    begins = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in begins + ends:  # torch creates the underlying hipEvent_t on first record
+        ev.record()
+        assert ev.cuda_event, "event handle not materialised"
+    base = case.opt
+    opts = [case.fd.options(force_num_splits=base.force_num_splits if base else 0,
+                            force_chunk=base.force_chunk if base else 0,
+                            split_begin_event=begins[i], split_end_event=ends[i]) for i in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        case.step(i, opts[i])
+    torch.cuda.synchronize()
+    split_ms = [b.elapsed_time(e) for b, e in zip(begins, ends)]
+    split_ms.sort()
+    return {"wall_s": wall, "split_mean_s": sum(split_ms) / len(split_ms) / 1e3,
+            "split_median_s": split_ms[len(split_ms) // 2] / 1e3}
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The float64 oracle as it stands, timed on this host over a bounded sample."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    d = w.make()
+    if w.kind == "single":
+        heads = list(range(w.H))
+        n_done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            h = heads[n_done % len(heads)]
+            oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=[h])
+            n_done += 1
+        el = time.perf_counter() - t0
+        sample = f"{n_done} single-head decodes of {w.name} (S={w.S}), {el:.1f} s"
+        step_s = el / n_done * w.H
+    else:
+        lens = d["seq_lens"].numpy()
+        n_done, tokens_done = 0, 0
+        rng = np.random.default_rng(0)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            b = int(rng.integers(w.B))
+            oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                          d["page_size"], d["scale"], pairs=[(b, h) for h in range(w.H)])
+            n_done += 1
+            tokens_done += int(lens[b])
+        el = time.perf_counter() - t0
+        sample = f"{n_done} whole sequences (all {w.H} heads) of {w.name}, {el:.1f} s"
+        step_s = el / tokens_done * float(lens.sum())
+    kv_bytes = w.kv_bytes()
+    return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "us_per_step": round(step_s * 1e6, 1)}
+
+
+def copy_probe(nbytes: int, steps: int) -> None:
+    """A plain device-to-device copy of known size (for scaling FETCH_SIZE/WRITE_SIZE)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--chunk", type=int, default=0, help="force tokens per split (multiple of 64)")
+    ap.add_argument("--sweep", action="store_true", help="also time the pages' KV-length sweep (4k..128k)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return 0
+
+    from decode_attention_13_amd.inputs import WORKLOADS, sweep_workload
+    w = WORKLOADS[args.workload]
+    case = Case(w, args.chunk)
+    t = time_steps(case, args.steps, args.warmup)
+    step_s = t["wall_s"]
+    split_s = t["split_mean_s"]
+    achieved = case.kv_bytes / split_s / 1e9
+    traffic = load_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(case.kv_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 6),
+        "us_per_step": round(step_s * 1e6, 3),
+        "frac_of_peak": round(case.kv_bytes / step_s / 1e9 / PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "kv_bytes": case.kv_bytes, "plan": case.plan, "kv_copies": case.copies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
+                     "kernel": SPLIT_KERNEL, "kernel_us_mean": round(split_s * 1e6, 3),
+                     "kernel_us_median": round(t["split_median_s"] * 1e6, 3),
+                     "bytes_per_launch": case.kv_bytes,
+                     "bytes_per_unit": case.kv_bytes // case.units, "units_per_launch": case.units},
+    }
+    del case
+    torch.cuda.empty_cache()
+    if args.sweep:
+        sweep = []
+        for S in SWEEP:
+            c = Case(sweep_workload(S))
+            ts = time_steps(c, max(20, args.steps // 4), 5)
+            sweep.append({"S": S, "us_per_step": round(ts["wall_s"] * 1e6, 2),
+                          "GBps": round(c.kv_bytes / ts["wall_s"] / 1e9, 1),
+                          "split_kernel_GBps": round(c.kv_bytes / ts["split_mean_s"] / 1e9, 1)})
+            log(f"sweep S={S}: {sweep[-1]}")
+            del c
+            torch.cuda.empty_cache()
+        line["sweep"] = sweep
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

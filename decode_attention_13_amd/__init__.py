@@ -1,0 +1,18 @@
+"""Split-KV decode attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libfd.so`` (HIP kernels behind the C ABI declared in
+``include/fd.h``); ``binding`` marshals torch tensors into it. The library is
+loaded on first use and its absence is an error, never a fallback.
+"""
+from .binding import (  # noqa: F401
+    FdError,
+    FdOptions,
+    decode_plan,
+    device_num_cus,
+    fd_decode,
+    fd_paged_decode,
+    lib,
+    options,
+    paged_plan,
+    workspace_views,
+)

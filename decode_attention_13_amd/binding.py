@@ -1,0 +1,234 @@
+"""ctypes binding of ``libfd.so`` (include/fd.h): argument marshalling only.
+
+Every step of the decode runs in the HIP kernels behind the C ABI. This module
+turns torch tensors into pointers, sizes and a dtype code, allocates the
+workspace with torch when the caller does not pass one, and raises on any
+non-zero status. There is no fallback: if the library is not built, the first
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfd.so")
+
+FD_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPE_NAMES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+HEAD_DIM = 128
+CHUNK_QUANTUM = 64
+
+
+class FdOptions(ctypes.Structure):
+    _fields_ = [("force_num_splits", ctypes.c_int), ("force_chunk", ctypes.c_int), ("force_kernel", ctypes.c_int),
+                ("reserved", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
+                ("split_end_event", ctypes.c_void_p)]
+
+
+class FdPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("heads_per_group", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("num_splits", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
+                ("grid_z", ctypes.c_int), ("threads", ctypes.c_int), ("merge", ctypes.c_int),
+                ("reserved", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("ws_lse_offset", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+# name -> (restype, argtypes); mirrors include/fd.h
+SIGNATURES = {
+    "fd_device_num_cus": (ctypes.c_int, []),
+    "fd_decode_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.POINTER(FdOptions), ctypes.POINTER(FdPlan)]),
+    "fd_paged_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                                     ctypes.POINTER(FdOptions), ctypes.POINTER(FdPlan)]),
+    "fd_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(FdOptions),
+                                 ctypes.c_void_p]),
+    "fd_paged_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_float,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(FdOptions),
+                                       ctypes.c_void_p]),
+    "fd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fd_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_13_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise FdError(status, L.fd_status_string(status).decode(), L.fd_last_error().decode())
+
+
+def options(force_num_splits: int = 0, force_chunk: int = 0, kernel: str | int = "auto",
+            split_begin_event=None, split_end_event=None) -> FdOptions:
+    """An ``fd_options`` block; events are ``torch.cuda.Event`` objects (or raw handles)."""
+    def handle(ev):
+        if ev is None:
+            return None
+        return ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    return FdOptions(int(force_num_splits), int(force_chunk), k, 0, handle(split_begin_event),
+                     handle(split_end_event))
+
+
+def _opt_ptr(opt):
+    return ctypes.byref(opt) if opt is not None else None
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, str):
+        dt = DTYPE_NAMES[dt]
+    if dt not in FD_DTYPE:
+        raise TypeError(f"unsupported dtype {dt}")
+    return FD_DTYPE[dt]
+
+
+def device_num_cus() -> int:
+    return int(lib().fd_device_num_cus())
+
+
+def decode_plan(H: int, Hkv: int, S: int, dtype, num_cus: int = 0, opt: FdOptions | None = None) -> dict:
+    p = FdPlan()
+    _check(lib().fd_decode_plan(H, Hkv, S, HEAD_DIM, _dtype_code(dtype), num_cus, _opt_ptr(opt), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def paged_plan(B: int, H: int, Hkv: int, dtype, page_size: int, max_seq_len: int, total_kv: int = 0,
+               num_cus: int = 0, opt: FdOptions | None = None) -> dict:
+    p = FdPlan()
+    _check(lib().fd_paged_plan(B, H, Hkv, HEAD_DIM, _dtype_code(dtype), page_size, max_seq_len, total_kv, num_cus,
+                               _opt_ptr(opt), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _workspace(ws, need: int, device) -> tuple[int, int, torch.Tensor | None]:
+    if need == 0:
+        return (ws.data_ptr() if ws is not None else 0), (ws.numel() * ws.element_size() if ws is not None else 0), None
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), ws.numel() * ws.element_size(), ws
+
+
+def fd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+              scale: float | None = None, ws: torch.Tensor | None = None, opt: FdOptions | None = None,
+              stream=None) -> torch.Tensor:
+    """Single decode over a contiguous cache: q [H, D], k/v [S, Hkv, D] -> o [H, D]."""
+    H, D = q.shape
+    S, Hkv, Dk = k.shape
+    if v.shape != k.shape or Dk != D:
+        raise ValueError("k and v must both be [S, Hkv, D] with q's D")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, q.dtype)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = _dtype_code(q.dtype)
+    plan = decode_plan(H, Hkv, S, q.dtype, 0, opt)
+    wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    _check(lib().fd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), H, Hkv, S, D, dt, float(scale),
+                           wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
+    return o
+
+
+def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, page_size: int | None = None, o: torch.Tensor | None = None,
+                    scale: float | None = None, max_seq_len: int | None = None, total_kv: int = 0,
+                    ws: torch.Tensor | None = None, opt: FdOptions | None = None, stream=None) -> torch.Tensor:
+    """Batched paged GQA decode: q [B, H, D], caches [num_pages, page_size, Hkv, D],
+    block_table [B, max_blocks] int32, seq_lens [B] int32 -> o [B, H, D].
+
+    ``max_seq_len`` must bound every entry of ``seq_lens``; if omitted it is read
+    from the device (a synchronising copy).
+    """
+    B, H, D = q.shape
+    num_pages, ps, Hkv, Dk = k_cache.shape
+    if page_size is None:
+        page_size = ps
+    if v_cache.shape != k_cache.shape or Dk != D or ps != page_size:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, D]")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n, q.dtype)
+    _require(block_table, "block_table", torch.int32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    max_blocks = block_table.shape[1]
+    dt = _dtype_code(q.dtype)
+    eff_max = min(int(max_seq_len), max_blocks * page_size)
+    plan = paged_plan(B, H, Hkv, q.dtype, page_size, eff_max, int(total_kv), 0, opt)
+    wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    _check(lib().fd_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                 seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
+                                 num_pages, max_blocks, int(max_seq_len), int(total_kv), dt, wp or None, wb,
+                                 _opt_ptr(opt), _stream_handle(stream)))
+    return o
+
+
+def workspace_views(ws: torch.Tensor, plan: dict, B: int, H: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """(ws_o [B, H, num_splits, D], ws_lse [B, H, num_splits]) float32 views of a workspace."""
+    n = plan["num_splits"]
+    rows = B * H * n
+    o = ws[: rows * HEAD_DIM * 4].view(torch.float32).view(B, H, n, HEAD_DIM)
+    off = plan["ws_lse_offset"]
+    lse = ws[off: off + rows * 4].view(torch.float32).view(B, H, n)
+    return o, lse

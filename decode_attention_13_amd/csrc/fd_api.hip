@@ -1,0 +1,327 @@
+// fd_api.hip -- the C ABI of include/fd.h: host-side validation, the split
+// planner and the kernel launches. Nothing here allocates device memory or
+// synchronises; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fd.h"
+#include "fd_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fd_status fail(fd_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2_exact(int x) {  // log2 of a power of two, -1 otherwise
+    if (x <= 0 || (x & (x - 1)) != 0) return -1;
+    int n = 0;
+    while ((1 << n) < x) ++n;
+    return n;
+}
+
+long long pow2_floor(long long x) {
+    long long p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+
+// Planner constants.
+//  - Workgroups aimed at per compute unit: a split-kernel workgroup is 4 waves
+//    whose register double buffer keeps 8 KB of K/V in flight per wave, so a
+//    few resident workgroups per CU keep the HBM queues full; enough of them
+//    also leave room for the sequence-length tail.
+//  - Chunk bounds: long enough to amortise a workgroup's start (q load, first
+//    round trip to HBM) and its partial write, short enough to spread short
+//    caches over the chip.
+constexpr int kTargetWgsPerCu = 4;
+constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 16384;
+constexpr int kMaxSplits = 4096;
+
+std::mutex g_cu_mutex;
+std::vector<int> g_cu_cache;
+
+int pick_heads_per_group(int G) {
+    for (int gt : {8, 4, 2, 1})
+        if (G % gt == 0) return gt;
+    return 1;
+}
+
+fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_options *opt) {
+    if (B < 1 || H < 1 || Hkv < 1) return fail(FD_ERR_INVALID_ARG, "B, H and Hkv must be >= 1 (got %d, %d, %d)", B, H, Hkv);
+    if (H % Hkv != 0) return fail(FD_ERR_INVALID_ARG, "H (%d) must be a multiple of Hkv (%d)", H, Hkv);
+    if (D != FD_HEAD_DIM) return fail(FD_ERR_UNSUPPORTED, "head dim %d unsupported (only %d)", D, FD_HEAD_DIM);
+    if (dtype != FD_DTYPE_F32 && dtype != FD_DTYPE_F16 && dtype != FD_DTYPE_BF16)
+        return fail(FD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (opt) {
+        if (opt->force_num_splits < 0 || opt->force_chunk < 0)
+            return fail(FD_ERR_INVALID_ARG, "negative force_num_splits/force_chunk");
+        if (opt->force_chunk > 0 && opt->force_chunk % FD_CHUNK_QUANTUM != 0)
+            return fail(FD_ERR_INVALID_ARG, "force_chunk %d is not a multiple of %d", opt->force_chunk,
+                        FD_CHUNK_QUANTUM);
+        if (opt->force_kernel < FD_KERNEL_AUTO || opt->force_kernel > FD_KERNEL_MFMA)
+            return fail(FD_ERR_INVALID_ARG, "unknown force_kernel %d", opt->force_kernel);
+        if (opt->reserved != 0) return fail(FD_ERR_INVALID_ARG, "fd_options.reserved must be 0");
+    }
+    return FD_OK;
+}
+
+// Shared planner. `max_len` is the longest sequence, `total` the sum of the
+// lengths (one sequence for contiguous decode), `page_size` 0 when contiguous.
+fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long long total, int page_size,
+                    int num_cus, const fd_options *opt, fd_plan *p) {
+    (void)dtype;
+    const int G = H / Hkv;
+    const int force_kernel = opt ? opt->force_kernel : FD_KERNEL_AUTO;
+    if (force_kernel == FD_KERNEL_MFMA)
+        return fail(FD_ERR_UNSUPPORTED, "the matrix-core split kernel is not available in this build");
+    const int gt = pick_heads_per_group(G);
+    const long long slices = (long long)Hkv * (G / gt);
+
+    long long chunk;
+    if (opt && opt->force_chunk > 0) {
+        chunk = opt->force_chunk;
+    } else if (opt && opt->force_num_splits > 0) {
+        const long long per = ((long long)std::max(max_len, 1) + opt->force_num_splits - 1) / opt->force_num_splits;
+        chunk = (per + FD_CHUNK_QUANTUM - 1) / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
+    } else {
+        // Token-rows over all workgroups divided by the workgroups wanted,
+        // rounded down to a power of two, then clamped.
+        const long long work = std::max(total, 1LL) * slices;
+        const long long target = (long long)num_cus * kTargetWgsPerCu;
+        chunk = pow2_floor(std::max(1LL, work / target));
+        chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
+    }
+    if (page_size > 0) {  // the split's slice of the block table must fit the LDS stage
+        const long long cap = (long long)(fd::kMaxSplitPages - 1) * page_size / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
+        if (chunk > cap) {
+            if (opt && opt->force_chunk > 0)
+                return fail(FD_ERR_INVALID_ARG, "force_chunk %d spans more than %d pages of %d tokens",
+                            opt->force_chunk, fd::kMaxSplitPages - 1, page_size);
+            chunk = std::max<long long>(cap, FD_CHUNK_QUANTUM);
+        }
+    }
+    long long splits = std::max(1LL, ((long long)max_len + chunk - 1) / chunk);
+    if (splits > kMaxSplits) {
+        chunk = ((long long)max_len + kMaxSplits - 1) / kMaxSplits;
+        chunk = (chunk + FD_CHUNK_QUANTUM - 1) / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
+        if (page_size > 0 && chunk > (long long)(fd::kMaxSplitPages - 1) * page_size)
+            return fail(FD_ERR_UNSUPPORTED, "sequence of %d tokens needs more than %d splits", max_len, kMaxSplits);
+        splits = std::max(1LL, ((long long)max_len + chunk - 1) / chunk);
+    }
+
+    std::memset(p, 0, sizeof(*p));
+    p->kernel = FD_KERNEL_VALU;
+    p->heads_per_group = gt;
+    p->chunk = (int)chunk;
+    p->num_splits = (int)splits;
+    p->grid_x = (int)splits;
+    p->grid_y = (int)slices;
+    p->grid_z = B;
+    p->threads = 256;
+    p->merge = splits > 1 ? 1 : 0;
+    if (p->merge) {
+        const size_t rows = (size_t)B * H * splits;
+        const size_t o_bytes = rows * FD_HEAD_DIM * sizeof(float);
+        p->ws_lse_offset = (o_bytes + 255) / 256 * 256;
+        p->workspace_bytes = p->ws_lse_offset + rows * sizeof(float);
+    }
+    return FD_OK;
+}
+
+fd_status resolve_cus(int *num_cus) {
+    if (*num_cus > 0) return FD_OK;
+    if (*num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus must be >= 0");
+    const int n = fd_device_num_cus();
+    if (n < 1) return fail(FD_ERR_DEVICE, "cannot query the compute units of the current device");
+    *num_cus = n;
+    return FD_OK;
+}
+
+fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a, fd::MergeArgs &m, int B,
+              void *ws, size_t ws_bytes, const fd_options *opt, hipStream_t stream) {
+    if (plan.merge) {
+        if (ws == nullptr || ws_bytes < plan.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", plan.workspace_bytes, ws_bytes,
+                        ws == nullptr ? " (NULL)" : "");
+        if (!aligned16(ws)) return fail(FD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        a.ws_o = reinterpret_cast<float *>(ws);
+        a.ws_lse = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + plan.ws_lse_offset);
+        a.direct = 0;
+    } else {
+        a.ws_o = nullptr;
+        a.ws_lse = nullptr;
+        a.direct = 1;
+    }
+    a.chunk = plan.chunk;
+    a.num_splits = plan.num_splits;
+    fd::LaunchShape shape{dim3(plan.grid_x, plan.grid_y, plan.grid_z), dim3(plan.threads)};
+
+    if (opt && opt->split_begin_event) {
+        if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_begin_event), stream) != hipSuccess)
+            return fail(FD_ERR_LAUNCH, "hipEventRecord(split_begin_event) failed");
+    }
+    hipError_t e = fd::launch_split_valu(dtype, plan.heads_per_group, paged, shape, a, stream);
+    if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
+    if (opt && opt->split_end_event) {
+        if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_end_event), stream) != hipSuccess)
+            return fail(FD_ERR_LAUNCH, "hipEventRecord(split_end_event) failed");
+    }
+    if (plan.merge) {
+        m.ws_o = a.ws_o;
+        m.ws_lse = a.ws_lse;
+        m.chunk = plan.chunk;
+        m.num_splits = plan.num_splits;
+        e = fd::launch_merge(dtype, paged, B, m, stream);
+        if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "merge kernel launch: %s", hipGetErrorString(e));
+    }
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_device_num_cus(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if ((int)g_cu_cache.size() <= dev) g_cu_cache.resize(dev + 1, 0);
+    if (g_cu_cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+        g_cu_cache[dev] = n;
+    }
+    return g_cu_cache[dev];
+}
+
+fd_status fd_decode_plan(int H, int Hkv, int S, int D, fd_dtype dtype, int num_cus, const fd_options *opt,
+                         fd_plan *out) {
+    if (!out) return fail(FD_ERR_INVALID_ARG, "out is NULL");
+    fd_status s = check_common(1, H, Hkv, D, dtype, opt);
+    if (s != FD_OK) return s;
+    if (S < 0) return fail(FD_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
+    if ((s = resolve_cus(&num_cus)) != FD_OK) return s;
+    return make_plan(1, H, Hkv, dtype, S, S, 0, num_cus, opt, out);
+}
+
+fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_size, int max_seq_len,
+                        long long total_kv, int num_cus, const fd_options *opt, fd_plan *out) {
+    if (!out) return fail(FD_ERR_INVALID_ARG, "out is NULL");
+    fd_status s = check_common(B, H, Hkv, D, dtype, opt);
+    if (s != FD_OK) return s;
+    if (ilog2_exact(page_size) < 0 || page_size > 1024)
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]", page_size);
+    if (max_seq_len < 0) return fail(FD_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+    if ((s = resolve_cus(&num_cus)) != FD_OK) return s;
+    const long long total = total_kv > 0 ? total_kv : (long long)B * max_seq_len;
+    return make_plan(B, H, Hkv, dtype, max_seq_len, total, page_size, num_cus, opt, out);
+}
+
+fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
+                    fd_dtype dtype, float scale, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+    fd_status s = check_common(1, H, Hkv, D, dtype, opt);
+    if (s != FD_OK) return s;
+    if (S < 0) return fail(FD_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
+    if (!q || !o || (S > 0 && (!k || !v))) return fail(FD_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(FD_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    fd_plan plan;
+    if ((s = fd_decode_plan(H, Hkv, S, D, dtype, 0, opt, &plan)) != FD_OK) return s;
+
+    fd::SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = o;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.G = H / Hkv;
+    a.max_len = S;
+    a.scale_log2 = scale * fd::kLog2eHost;
+    fd::MergeArgs m{};
+    m.out = o;
+    m.H = H;
+    m.max_len = S;
+    return run(plan, dtype, false, a, m, 1, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream));
+}
+
+fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
+                          const int32_t *seq_lens, int page_size, void *o, float scale, int B, int H, int Hkv, int D,
+                          int num_pages, int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
+                          void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+    fd_status s = check_common(B, H, Hkv, D, dtype, opt);
+    if (s != FD_OK) return s;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+        return fail(FD_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and o must not be NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return fail(FD_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return fail(FD_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
+    if (num_pages < 1 || max_blocks < 1) return fail(FD_ERR_INVALID_ARG, "num_pages and max_blocks must be >= 1");
+    const int shift = ilog2_exact(page_size);
+    if (shift < 0 || page_size > 1024)
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]", page_size);
+    if (max_seq_len < 0) return fail(FD_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+    // Every length is clamped to what the table can address.
+    const long long addressable = (long long)max_blocks * page_size;
+    const int eff_max = (int)std::min<long long>(max_seq_len, addressable);
+    fd_plan plan;
+    if ((s = fd_paged_plan(B, H, Hkv, D, dtype, page_size, eff_max, total_kv, 0, opt, &plan)) != FD_OK) return s;
+
+    fd::SplitArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.out = o;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.G = H / Hkv;
+    a.max_len = eff_max;
+    a.page_shift = shift;
+    a.max_blocks = max_blocks;
+    a.num_pages = num_pages;
+    a.scale_log2 = scale * fd::kLog2eHost;
+    fd::MergeArgs m{};
+    m.seq_lens = seq_lens;
+    m.out = o;
+    m.H = H;
+    m.max_len = eff_max;
+    return run(plan, dtype, true, a, m, B, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char *fd_status_string(fd_status s) {
+    switch (s) {
+        case FD_OK: return "FD_OK";
+        case FD_ERR_INVALID_ARG: return "FD_ERR_INVALID_ARG";
+        case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
+        case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
+        case FD_ERR_DEVICE: return "FD_ERR_DEVICE";
+        case FD_ERR_LAUNCH: return "FD_ERR_LAUNCH";
+    }
+    return "FD_ERR_UNKNOWN";
+}
+
+const char *fd_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// fd_internal.h -- argument blocks shared by the C-ABI layer and the kernel
+// launchers. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fd.h"
+
+namespace fd {
+
+// Most physical pages one split may touch: the paged split kernel stages the
+// split's block-table slice in LDS. The planner keeps chunk / page_size + 1
+// within this bound.
+constexpr int kMaxSplitPages = 1024;
+
+constexpr float kLog2eHost = 1.4426950408889634f;  // log2(e), folded into the scale on the host
+
+struct SplitArgs {
+    const void *q;          // [B, H, D]
+    const void *k;          // contiguous [S, Hkv, D] or cache [num_pages, page_size, Hkv, D]
+    const void *v;
+    const int32_t *block_table;  // [B, max_blocks] (paged)
+    const int32_t *seq_lens;     // [B] (paged)
+    float *ws_o;            // [B, H, num_splits, D]
+    float *ws_lse;          // [B, H, num_splits]
+    void *out;              // [B, H, D] (direct mode)
+    int H, Hkv, G;          // G = H / Hkv
+    int max_len;            // contiguous: S; paged: clamp bound for seq_lens
+    int chunk;              // tokens per split
+    int num_splits;
+    int page_shift;         // log2(page_size)
+    int max_blocks;
+    int num_pages;
+    int direct;             // 1: write o (single split), 0: write partials
+    float scale_log2;       // scale * log2(e)
+};
+
+struct MergeArgs {
+    const float *ws_o;
+    const float *ws_lse;
+    const int32_t *seq_lens;  // paged only
+    void *out;
+    int H;
+    int max_len;              // contiguous: S; paged: clamp bound for seq_lens
+    int chunk;
+    int num_splits;
+};
+
+struct LaunchShape {
+    dim3 grid;
+    dim3 block;
+};
+
+// Each returns hipSuccess or the launch error. `gt` = heads per workgroup.
+hipError_t launch_split_valu(fd_dtype dtype, int gt, bool paged, const LaunchShape &shape, const SplitArgs &a,
+                             hipStream_t stream);
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, bool paged, const LaunchShape &shape, const SplitArgs &a,
+                             hipStream_t stream);
+hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, hipStream_t stream);
+
+}  // namespace fd

@@ -1,0 +1,278 @@
+// fd_split_valu.hip -- split kernel on the vector ALUs (gfx950, wave64).
+//
+// One workgroup of 4 waves computes one (sequence b, KV split, group of GT
+// query heads sharing KV head kvh). It streams the split's K/V rows straight
+// into registers with 16-byte loads: a 16-lane DPP row owns one 256-byte bf16
+// row (512-byte fp32 row as two loads), so a wave covers four rows per load
+// instruction and every load fills whole 128-byte lines. Each wave walks the
+// split in tiles of 16 tokens (4 rows per 16-lane group), interleaved with the
+// other waves, and prefetches its next tile's K and V into a second register
+// set before computing the current one (a register double buffer; no LDS is
+// needed because every lane consumes exactly the bytes it loaded).
+//
+// Per row: q.k on v_dot2 (16-bit) or FMA (fp32) over the lane's 8 elements,
+// a 4-step DPP butterfly across the row, then the online-softmax update in
+// the log2 domain ("FlashAttention 与推理算子", section "FlashAttention：分块 +
+// online softmax"; the exp2 form with scale*log2(e) folded into the scores as
+// in "[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节")
+// and the P.V accumulation in fp32. The 16 per-group states of a workgroup
+// are merged once at the end (DPP-free lane shuffles inside a wave, LDS across
+// waves) and written as a normalised partial plus its natural-log lse, or,
+// when one split covers the sequence, as the final output.
+#include "fd_device.h"
+#include "fd_internal.h"
+
+namespace fd {
+
+namespace {
+
+constexpr int kThreads = 256;          // 4 waves
+constexpr int kRows = 4;               // rows per 16-lane group per wave tile
+constexpr int kWaveTile = 4 * kRows;   // tokens per wave tile
+constexpr int kWaves = kThreads / 64;
+
+template <typename T, int GT, bool PAGED>
+__global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
+    using E = Elem<T>;
+    constexpr int NL = E::kLoads;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4;
+    const int c = lane & 15;
+    const int split = blockIdx.x;
+    const int slices = a.G / GT;
+    const int kvh = blockIdx.y / slices;
+    const int h0 = kvh * a.G + (blockIdx.y - kvh * slices) * GT;
+    const int b = blockIdx.z;
+
+    __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
+    __shared__ float s_m[kWaves][GT];
+    __shared__ float s_l[kWaves][GT];
+    __shared__ float s_acc[kWaves][GT][kHeadDim];
+
+    int L = a.max_len;
+    if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
+    const int t_begin = split * a.chunk;
+    if (t_begin >= L) {  // uniform over the workgroup
+        if (a.direct && split == 0) {  // empty sequence: o = 0
+            T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
+            for (int i = threadIdx.x; i < GT * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
+        }
+        return;
+    }
+    const int t_end = min(t_begin + a.chunk, L);
+
+    int page_first = 0;
+    if (PAGED) {
+        page_first = t_begin >> a.page_shift;
+        const int n_pages = ((t_end - 1) >> a.page_shift) - page_first + 1;
+        const int32_t *row = a.block_table + (size_t)b * a.max_blocks + page_first;
+        for (int i = threadIdx.x; i < n_pages; i += kThreads) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
+        __syncthreads();
+    }
+
+    const T *kbase = reinterpret_cast<const T *>(a.k);
+    const T *vbase = reinterpret_cast<const T *>(a.v);
+    const int page_mask = (1 << a.page_shift) - 1;
+    auto row_offset = [&](int t) -> size_t {  // element offset of (token t, KV head kvh, d = 0)
+        if constexpr (PAGED) {
+            const int page = s_pages[(t >> a.page_shift) - page_first];
+            const size_t slot_row = ((size_t)page << a.page_shift) + (size_t)(t & page_mask);
+            return (slot_row * a.Hkv + kvh) * kHeadDim;
+        } else {
+            return ((size_t)t * a.Hkv + kvh) * kHeadDim;
+        }
+    };
+
+    // q fragments of the GT heads: fp32 for fp32 inputs, packed pairs otherwise.
+    float qf[GT][8];
+    uint32_t qp[GT][4];
+    const T *qbase = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.H + h0) * kHeadDim;
+#pragma unroll
+    for (int gi = 0; gi < GT; ++gi) {
+        uint4 x[NL];
+#pragma unroll
+        for (int pc = 0; pc < NL; ++pc) x[pc] = load16(qbase + gi * kHeadDim + E::offset(c, pc));
+        if constexpr (NL == 2) {
+            E::unpack(x, qf[gi]);
+        } else {
+            qp[gi][0] = x[0].x;
+            qp[gi][1] = x[0].y;
+            qp[gi][2] = x[0].z;
+            qp[gi][3] = x[0].w;
+        }
+    }
+
+    float m[GT], l[GT], acc[GT][8];
+#pragma unroll
+    for (int gi = 0; gi < GT; ++gi) {
+        m[gi] = -INFINITY;
+        l[gi] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
+    }
+
+    const int ntiles = (t_end - t_begin + kWaveTile - 1) / kWaveTile;
+
+    auto load_tile = [&](int j, uint4 (&kx)[kRows][NL], uint4 (&vx)[kRows][NL]) {
+        const int t0 = t_begin + j * kWaveTile + grp * kRows;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const size_t off = row_offset(min(t0 + r, t_end - 1));  // tail rows re-read a valid row, then masked
+#pragma unroll
+            for (int pc = 0; pc < NL; ++pc) {
+                kx[r][pc] = load_stream16(kbase + off + E::offset(c, pc));
+                vx[r][pc] = load_stream16(vbase + off + E::offset(c, pc));
+            }
+        }
+    };
+
+    auto compute_tile = [&](int j, const uint4 (&kx)[kRows][NL], const uint4 (&vx)[kRows][NL]) {
+        const int t0 = t_begin + j * kWaveTile + grp * kRows;
+        float p[GT][kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const bool valid = t0 + r < t_end;
+#pragma unroll
+            for (int gi = 0; gi < GT; ++gi) {
+                const float d = row16_sum(E::dot(qf[gi], qp[gi], kx[r]));
+                p[gi][r] = valid ? d * a.scale_log2 : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < GT; ++gi) {
+            float mt = p[gi][0];
+#pragma unroll
+            for (int r = 1; r < kRows; ++r) mt = fmaxf(mt, p[gi][r]);
+            const float m_new = fmaxf(m[gi], mt);
+            const float mu = finite_or_zero(m_new);
+            const float alpha = exp2_fast(m[gi] - mu);
+            l[gi] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[gi][e] *= alpha;
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                p[gi][r] = exp2_fast(p[gi][r] - mu);
+                l[gi] += p[gi][r];
+            }
+            m[gi] = m_new;
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float vf[8];
+            E::unpack(vx[r], vf);
+#pragma unroll
+            for (int gi = 0; gi < GT; ++gi)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[gi][e] = __builtin_fmaf(p[gi][r], vf[e], acc[gi][e]);
+        }
+    };
+
+    uint4 kA[kRows][NL], vA[kRows][NL], kB[kRows][NL], vB[kRows][NL];
+    int j = wave;
+    if (j < ntiles) load_tile(j, kA, vA);
+    while (j < ntiles) {
+        if (j + kWaves < ntiles) load_tile(j + kWaves, kB, vB);
+        compute_tile(j, kA, vA);
+        j += kWaves;
+        if (j >= ntiles) break;
+        if (j + kWaves < ntiles) load_tile(j + kWaves, kA, vA);
+        compute_tile(j, kB, vB);
+        j += kWaves;
+    }
+
+    // Merge the four 16-lane groups of each wave: lanes c, c^16, c^32, c^48 own
+    // the same head-dim elements.
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+#pragma unroll
+        for (int gi = 0; gi < GT; ++gi) {
+            const float mo = __shfl_xor(m[gi], mask, 64);
+            const float lo = __shfl_xor(l[gi], mask, 64);
+            const float M = fmaxf(m[gi], mo);
+            const float mu = finite_or_zero(M);
+            const float a1 = exp2_fast(m[gi] - mu);
+            const float a2 = exp2_fast(mo - mu);
+            l[gi] = a1 * l[gi] + a2 * lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xo = __shfl_xor(acc[gi][e], mask, 64);
+                acc[gi][e] = a1 * acc[gi][e] + a2 * xo;
+            }
+            m[gi] = M;
+        }
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int gi = 0; gi < GT; ++gi) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_acc[wave][gi][E::index(c, e)] = acc[gi][e];
+            if (c == 0) {
+                s_m[wave][gi] = m[gi];
+                s_l[wave][gi] = l[gi];
+            }
+        }
+    }
+    __syncthreads();
+
+    // Merge the waves and store: one thread per (head, element).
+    for (int i = threadIdx.x; i < GT * kHeadDim; i += kThreads) {
+        const int gi = i / kHeadDim;
+        const int d = i - gi * kHeadDim;
+        float M = s_m[0][gi];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gi]);
+        const float mu = finite_or_zero(M);
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wgt = exp2_fast(s_m[w][gi] - mu);
+            lsum = __builtin_fmaf(wgt, s_l[w][gi], lsum);
+            o = __builtin_fmaf(wgt, s_acc[w][gi][d], o);
+        }
+        const float out = o / lsum;
+        const size_t bh = (size_t)b * a.H + h0 + gi;
+        if (a.direct) {
+            reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = E::store_cast(out);
+        } else {
+            const size_t row = bh * a.num_splits + split;
+            a.ws_o[row * kHeadDim + d] = out;
+            if (d == 0) a.ws_lse[row] = (M + log2_fast(lsum)) * kLn2;
+        }
+    }
+}
+
+template <typename T, int GT, bool PAGED>
+hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+    SplitArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, PAGED>), s.grid, s.block, args, 0,
+                           st);
+}
+
+template <typename T, bool PAGED>
+hipError_t launch_gt(int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+    switch (gt) {
+        case 1: return launch_one<T, 1, PAGED>(s, a, st);
+        case 2: return launch_one<T, 2, PAGED>(s, a, st);
+        case 4: return launch_one<T, 4, PAGED>(s, a, st);
+        case 8: return launch_one<T, 8, PAGED>(s, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_valu(fd_dtype dtype, int gt, bool paged, const LaunchShape &s, const SplitArgs &a,
+                             hipStream_t st) {
+    switch (dtype) {
+        case FD_DTYPE_F32: return paged ? launch_gt<float, true>(gt, s, a, st) : launch_gt<float, false>(gt, s, a, st);
+        case FD_DTYPE_F16:
+            return paged ? launch_gt<_Float16, true>(gt, s, a, st) : launch_gt<_Float16, false>(gt, s, a, st);
+        case FD_DTYPE_BF16:
+            return paged ? launch_gt<__bf16, true>(gt, s, a, st) : launch_gt<__bf16, false>(gt, s, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fd

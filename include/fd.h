@@ -1,0 +1,176 @@
+/*
+ * fd.h -- split-KV ("Flash-Decoding") single-query decode attention for AMD
+ * Instinct MI355X (gfx950). C ABI: plain pointers, sizes and status codes.
+ *
+ * What is computed. For every sequence b and query head h, with KV head
+ * g = h / (H / Hkv) (consecutive query heads share one KV head, as in the GQA
+ * paged decode kernel of "FlashAttention 与推理算子", section "一个分页 decode
+ * attention kernel（支持 GQA）") and the L_b keys and values of that head:
+ *
+ *     s_t = scale * q[b,h,:] . k[t,g,:]          t = 0 .. L_b - 1
+ *     o[b,h,:] = sum_t softmax(s)_t * v[t,g,:]
+ *
+ * i.e. S = Q K^T * scale, P = softmax(S), O = P V for one query row ("Flash
+ * Attention 与推理算子", section "标准注意力的问题"). The KV sequence is cut
+ * into splits of `chunk` tokens; a first kernel computes each split's
+ * normalised output and log-sum-exp with an online softmax, a second merges
+ * the splits by log-sum-exp ("[CUDA 优化实战] 纯手搓 flash decoding sm120",
+ * sections "1. flash decoding" and "2. kernel 实现细节"; "FlashAttention 与
+ * 推理算子", section "decode 阶段的并行：Flash-Decoding 与 split-K"). When one
+ * split covers the longest sequence the first kernel writes o directly and no
+ * merge runs. The result does not depend on the split count beyond rounding.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE memory owned by the caller, contiguous
+ *     row-major and 16-byte aligned. q, k, v and o share one dtype;
+ *     accumulation is fp32; o is rounded to its dtype to nearest-even.
+ *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the null
+ *     stream): no synchronisation, no allocation, no hidden state except a
+ *     cached compute-unit count per device. Thread-safe. Calls that share a
+ *     workspace must not overlap.
+ *   - Head dimension D must be 128 (FD_HEAD_DIM).
+ *   - Errors are returned as fd_status; nothing is launched when a host-side
+ *     check fails. fd_last_error() holds a message for the calling thread.
+ */
+#ifndef FD_H_
+#define FD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FD_HEAD_DIM 128
+#define FD_CHUNK_QUANTUM 64 /* a forced chunk must be a positive multiple of this */
+
+typedef enum fd_dtype {
+    FD_DTYPE_F32 = 0,
+    FD_DTYPE_F16 = 1,
+    FD_DTYPE_BF16 = 2
+} fd_dtype;
+
+typedef enum fd_status {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, H % Hkv != 0, bad option */
+    FD_ERR_UNSUPPORTED = 2, /* D != 128, page_size not a power of two in [1, 1024], unknown dtype */
+    FD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fd_plan.workspace_bytes */
+    FD_ERR_DEVICE = 4,      /* no current HIP device / attribute query failed */
+    FD_ERR_LAUNCH = 5       /* a kernel launch or event record returned an error */
+} fd_status;
+
+enum {
+    FD_KERNEL_AUTO = 0, /* planner's choice */
+    FD_KERNEL_VALU = 1, /* vector-ALU split kernel (any head group, every dtype) */
+    FD_KERNEL_MFMA = 2  /* matrix-core split kernel (f16/bf16, H/Hkv in {4, 8, 16}) */
+};
+
+/* Optional knobs; pass NULL for all defaults. Zero means "automatic". */
+typedef struct fd_options {
+    int force_num_splits; /* > 0: split the longest sequence into about this many splits */
+    int force_chunk;      /* > 0: tokens per split, a multiple of FD_CHUNK_QUANTUM (wins over force_num_splits) */
+    int force_kernel;     /* FD_KERNEL_* */
+    int reserved;         /* must be 0 */
+    void *split_begin_event; /* hipEvent_t recorded on `stream` right before the split kernel, or NULL */
+    void *split_end_event;   /* hipEvent_t recorded on `stream` right after the split kernel, or NULL */
+} fd_options;
+
+/* What a call with the same arguments would launch. */
+typedef struct fd_plan {
+    int kernel;          /* FD_KERNEL_VALU or FD_KERNEL_MFMA */
+    int heads_per_group; /* query heads one workgroup computes (they share one KV head) */
+    int chunk;           /* KV tokens per split */
+    int num_splits;      /* splits of the longest sequence = grid x */
+    int grid_x, grid_y, grid_z; /* split kernel grid: (splits, KV-head slices, sequences) */
+    int threads;         /* split kernel workgroup size */
+    int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: direct output */
+    int reserved;
+    size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
+    size_t ws_lse_offset;   /* byte offset of the lse array inside the workspace */
+} fd_plan;
+
+/*
+ * Workspace layout when merge == 1 (fp32, row-major, from byte 0):
+ *   ws_o  [B, H, num_splits, D]  normalised output of each split
+ *   ws_lse[B, H, num_splits]     natural-log log-sum-exp of each split's scores,
+ *                                at byte offset ws_lse_offset.
+ * Split s of sequence b covers tokens [s*chunk, min((s+1)*chunk, L_b)); only
+ * splits s < ceil(L_b / chunk) are written. The split kernel stores partials the
+ * way "[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节"
+ * describes (normalised output plus log-sum-exp per split).
+ */
+
+/* Compute units of the current HIP device (cached per device); -1 on error. */
+int fd_device_num_cus(void);
+
+/*
+ * Plan of fd_decode. num_cus > 0 uses that compute-unit count (pure host
+ * arithmetic, no GPU needed); num_cus == 0 queries the current device.
+ * Argument meaning as in fd_decode.
+ */
+fd_status fd_decode_plan(int H, int Hkv, int S, int D, fd_dtype dtype, int num_cus,
+                         const fd_options *opt, fd_plan *out);
+
+/* Plan of fd_paged_decode; arguments as there. */
+fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_size,
+                        int max_seq_len, long long total_kv, int num_cus,
+                        const fd_options *opt, fd_plan *out);
+
+/*
+ * Single decode over a contiguous KV cache ("[CUDA 优化实战] 纯手搓 flash
+ * decoding sm120", section "1. flash decoding": q [head, dim], kv [seq, head,
+ * dim]).
+ *   q  [H, D]          query, one row per head
+ *   k  [S, Hkv, D]     keys, token-major
+ *   v  [S, Hkv, D]     values, token-major
+ *   o  [H, D]          output, fully overwritten (S == 0 gives zeros)
+ *   scale              softmax scale (callers usually pass 1/sqrt(D))
+ *   ws, ws_bytes       caller-owned device workspace of at least
+ *                      fd_plan.workspace_bytes (may be NULL when that is 0)
+ *   opt                NULL or options; stream: hipStream_t or NULL.
+ */
+fd_status fd_decode(const void *q, const void *k, const void *v, void *o,
+                    int H, int Hkv, int S, int D, fd_dtype dtype, float scale,
+                    void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
+
+/*
+ * Batched decode over a paged KV cache with grouped-query heads
+ * ("FlashAttention 与推理算子", sections "PagedAttention" and "一个分页 decode
+ * attention kernel（支持 GQA）": token t of sequence b is slot t % page_size of
+ * physical page block_table[b][t / page_size]).
+ *   q            [B, H, D]
+ *   k_cache      [num_pages, page_size, Hkv, D]
+ *   v_cache      [num_pages, page_size, Hkv, D]
+ *   block_table  [B, max_blocks] int32, device; entries past ceil(L_b/page_size)
+ *                are never read (padding such as -1 is fine). Entries that are
+ *                read must lie in [0, num_pages); others are clamped into that
+ *                range (that sequence's output is then unspecified, but no
+ *                access leaves the cache).
+ *   seq_lens     [B] int32, device; L_b, clamped to [0, min(max_seq_len,
+ *                max_blocks * page_size)]; L_b == 0 gives o[b] = 0.
+ *   page_size    tokens per page, a power of two in [1, 1024]
+ *   o            [B, H, D], fully overwritten
+ *   max_seq_len  host-side upper bound of every L_b (sizes the grid; no
+ *                device-to-host read of seq_lens ever happens)
+ *   total_kv     host-side sum of L_b if known (> 0), else <= 0; used only to
+ *                size the splits
+ *   Other arguments as in fd_decode.
+ */
+fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_table, const int32_t *seq_lens, int page_size,
+                          void *o, float scale, int B, int H, int Hkv, int D, int num_pages,
+                          int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
+                          void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
+
+/* Static name of a status code. */
+const char *fd_status_string(fd_status s);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *fd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H_ */

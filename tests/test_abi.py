@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, plans
+with pure host arithmetic, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import decode_attention_13_amd as fd
+from decode_attention_13_amd import binding
+from decode_attention_13_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("fd_decode", "fd_paged_decode", "fd_decode_plan", "fd_paged_plan", "fd_status_string",
+                     "fd_last_error", "fd_device_num_cus"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(binding.SIGNATURES)
+
+
+def test_status_strings():
+    lib = fd.lib()
+    names = [lib.fd_status_string(i).decode() for i in range(6)]
+    assert names == ["FD_OK", "FD_ERR_INVALID_ARG", "FD_ERR_UNSUPPORTED", "FD_ERR_WORKSPACE", "FD_ERR_DEVICE",
+                     "FD_ERR_LAUNCH"]
+    assert lib.fd_status_string(99).decode() == "FD_ERR_UNKNOWN"
+
+
+def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
+    assert p["chunk"] % 64 == 0 and p["chunk"] >= 64
+    assert p["num_splits"] == max(1, -(-max_len // p["chunk"]))
+    assert p["grid_x"] == p["num_splits"] and p["grid_z"] == B
+    gt = p["heads_per_group"]
+    assert (H // Hkv) % gt == 0 and p["grid_y"] == Hkv * (H // Hkv) // gt
+    if p["merge"]:
+        rows = B * H * p["num_splits"]
+        assert p["ws_lse_offset"] >= rows * 128 * 4 and p["ws_lse_offset"] % 256 == 0
+        assert p["workspace_bytes"] == p["ws_lse_offset"] + rows * 4
+    else:
+        assert p["num_splits"] == 1 and p["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_plan_of_each_workload(name):
+    w = WORKLOADS[name]
+    if w.kind == "single":
+        p = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 256)
+        _check_plan(p, w.S, 1, w.H, w.Hkv)
+        assert p["grid_x"] * p["grid_y"] >= 16  # spreads over the chip
+    else:
+        L = w.seq_lens()
+        p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+        _check_plan(p, int(L.max()), w.B, w.H, w.Hkv)
+        assert p["heads_per_group"] == w.H // w.Hkv  # KV read once per group of q heads
+
+
+def test_plan_forced_splits_and_chunks():
+    for n in (1, 2, 3, 7, 1000):
+        p = fd.decode_plan(32, 32, 4099, "bf16", 256, fd.options(force_num_splits=n))
+        _check_plan(p, 4099, 1, 32, 32)
+        assert p["num_splits"] <= n
+    for c in (64, 192, 1024, 8192):
+        p = fd.decode_plan(32, 32, 4099, "bf16", 256, fd.options(force_chunk=c))
+        assert p["chunk"] == c and p["num_splits"] == -(-4099 // c)
+    # more CUs never means fewer splits
+    a = fd.decode_plan(32, 32, 131072, "bf16", 64)
+    b = fd.decode_plan(32, 32, 131072, "bf16", 256)
+    assert b["num_splits"] >= a["num_splits"]
+    # S = 0 still has one (empty) split that writes zeros
+    z = fd.decode_plan(8, 8, 0, "f32", 256)
+    assert z["num_splits"] == 1 and z["merge"] == 0
+
+
+def test_plan_paged_chunk_fits_block_table_stage():
+    for ps in (1, 2, 16, 64, 256, 1024):
+        p = fd.paged_plan(2, 8, 8, "bf16", ps, 1 << 20, 2 << 20, 256)
+        pages = p["chunk"] // ps + 1
+        assert pages <= 1024
+    with pytest.raises(fd.FdError) as e:
+        fd.paged_plan(2, 8, 8, "bf16", 1, 100000, 0, 256, fd.options(force_chunk=2048))
+    assert e.value.name == "FD_ERR_INVALID_ARG"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=6, Hkv=4), "FD_ERR_INVALID_ARG"),
+    (dict(D=64), "FD_ERR_UNSUPPORTED"),
+    (dict(S=-1), "FD_ERR_INVALID_ARG"),
+    (dict(dtype=7), "FD_ERR_UNSUPPORTED"),
+])
+def test_plan_rejects(kw, status):
+    args = dict(H=8, Hkv=8, S=16, D=128, dtype=0)
+    args.update(kw)
+    p = binding.FdPlan()
+    rc = fd.lib().fd_decode_plan(args["H"], args["Hkv"], args["S"], args["D"], args["dtype"], 256, None,
+                                 ctypes.byref(p))
+    assert fd.lib().fd_status_string(rc).decode() == status
+    assert fd.lib().fd_last_error().decode() != ""
+
+
+def test_options_are_validated():
+    for opt in (fd.options(force_chunk=100), fd.options(force_num_splits=-1), fd.options(kernel=5),
+                binding.FdOptions(0, 0, 0, 1, None, None)):
+        with pytest.raises(fd.FdError) as e:
+            fd.decode_plan(8, 8, 512, "f32", 256, opt)
+        assert e.value.name == "FD_ERR_INVALID_ARG"
+
+
+def test_decode_rejects_bad_pointers_without_a_device():
+    lib = fd.lib()
+    args = [None, 16, 16, 32, 8, 8, 512, 128, 0, 0.1, None, 0, None, None]
+    assert lib.fd_decode(*args) == 1  # q NULL
+    misaligned = [8, 16, 16, 32, 8, 8, 512, 128, 0, 0.1, None, 0, None, None]
+    assert lib.fd_decode(*misaligned) == 1
+    assert lib.fd_decode(16, 16, 16, 32, 8, 8, 512, 96, 0, 0.1, None, 0, None, None) == 2  # D
+    # page_size 24 is not a power of two
+    rc = lib.fd_paged_decode(16, 16, 16, 16, 16, 24, 16, 0.1, 2, 8, 8, 128, 4, 4, 64, 0, 2, None, 0, None, None)
+    assert lib.fd_status_string(rc).decode() == "FD_ERR_UNSUPPORTED"
+    rc = lib.fd_paged_decode(16, 16, 16, 18, 16, 16, 16, 0.1, 2, 8, 8, 128, 4, 4, 64, 0, 2, None, 0, None, None)
+    assert lib.fd_status_string(rc).decode() == "FD_ERR_INVALID_ARG"  # misaligned block table
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_is_reported():
+    assert fd.device_num_cus() == -1
+    with pytest.raises(fd.FdError) as e:
+        fd.decode_plan(8, 8, 512, "f32", 0)
+    assert e.value.name == "FD_ERR_DEVICE"

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerance (elementwise, the allclose convention): |gpu - ref| <= atol + rtol*|ref|
+with the unrounded float64 oracle as ref; bf16/f16 inputs: atol 2e-3, rtol 1e-2
+(fp32 accumulation, output rounded to the input dtype); fp32 inputs: 1e-5/1e-5.
+Addressing through the block table is checked bit-exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_13_amd as fd
+import oracle
+from decode_attention_13_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+DT = inputs.DTYPES
+
+
+def announce(msg: str) -> None:
+    """Name the case on the real stderr before its GPU step (survives a lost box)."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    fd.lib()
+    assert fd.device_num_cus() > 0
+    torch.cuda.set_device(0)
+    yield torch.device("cuda:0")
+    torch.cuda.synchronize()
+
+
+def assert_close(got, ref, dtype: str, what: str = ""):
+    got = got.detach().to(torch.float64).cpu().numpy() if hasattr(got, "detach") else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    atol, rtol = TOL[dtype]
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    msg = (f"{what}: max|err| {err.max():.3e}, max rel {rel.max():.3e}, "
+           f"{int(bad.sum())}/{bad.size} outside atol {atol} + rtol {rtol}")
+    assert not bad.any(), msg
+    return err.max()
+
+
+def to_dev(d: dict, dev) -> dict:
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def run_single(d, dev, opt=None, ws=None):
+    g = to_dev(d, dev)
+    o = fd.fd_decode(g["q"], g["k"], g["v"], scale=d["scale"], opt=opt, ws=ws)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_paged(d, dev, opt=None, ws=None, block_table=None):
+    g = to_dev(d, dev)
+    bt = block_table.to(dev) if block_table is not None else g["block_table"]
+    o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], bt, g["seq_lens"], d["page_size"],
+                           scale=d["scale"], max_seq_len=d["max_seq_len"], total_kv=d["total_kv"], opt=opt, ws=ws)
+    torch.cuda.synchronize()
+    return o
+
+
+# ------------------------------------------------------------------ pins on the GPU
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_worked_example(dtype, device):
+    """Scores [1, 3 | 2, 5] and scalar values [10, 20 | 30, 40] embedded at D = 128
+    (q = e_0, k[t, 0] = s_t): every output element is 36.8806 (the page's 36.88)."""
+    announce(f"worked example {dtype}")
+    s = [1.0, 3.0, 2.0, 5.0]
+    vals = [10.0, 20.0, 30.0, 40.0]
+    q = torch.zeros(1, 128)
+    q[0, 0] = 1
+    k = torch.zeros(4, 1, 128)
+    k[:, 0, 0] = torch.tensor(s)
+    v = torch.tensor(vals)[:, None, None].expand(4, 1, 128).contiguous()
+    d = {"q": q.to(DT[dtype]), "k": k.to(DT[dtype]), "v": v.to(DT[dtype]), "scale": 1.0}
+    o = run_single(d, device)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], 1.0)
+    assert abs(ref[0, 0] - 36.880566) < 1e-6
+    assert_close(o, ref, dtype, "worked example")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_key_is_bit_exact(dtype, device):
+    """S = 1: p = 1, l = 1, so o must equal v_0 bit for bit (also through a paged table)."""
+    announce(f"single key {dtype}")
+    d = inputs.single_inputs(8, 2, 1, 128, dtype, 31)
+    o = run_single(d, device)
+    want = d["v"][0].repeat_interleave(4, dim=0)
+    assert torch.equal(o.cpu(), want)
+    p = inputs.paged_inputs(3, 8, 2, 128, dtype, 16, [1, 1, 1], 32)
+    o = run_paged(p, device)
+    for b in range(3):
+        page = int(p["block_table"][b, 0])
+        assert torch.equal(o[b].cpu(), p["v_cache"][page, 0].repeat_interleave(4, dim=0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identical_keys_give_mean(dtype, device):
+    announce(f"identical keys {dtype}")
+    d = inputs.single_inputs(4, 4, 777, 128, dtype, 41)
+    d["k"] = d["k"][:1].expand(777, 4, 128).contiguous()
+    o = run_single(d, device)
+    mean = d["v"].to(torch.float64).mean(dim=0).numpy()
+    assert_close(o, mean, dtype, "mean of V")
+
+
+# ------------------------------------------------------------------ the five workloads
+
+
+def test_workload_f32_h8_s512(device):
+    w = inputs.WORKLOADS["decode_f32_h8_s512"]
+    announce(f"{w.name}")
+    d = w.make()
+    o = run_single(d, device)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    assert_close(o, ref, "f32", w.name)
+
+
+def test_workload_bf16_h32_s4096(device):
+    w = inputs.WORKLOADS["decode_bf16_h32_s4096"]
+    announce(f"{w.name}")
+    d = w.make()
+    o = run_single(d, device)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    assert_close(o, ref, "bf16", w.name)
+
+
+@pytest.fixture(scope="module")
+def long_peaked():
+    return inputs.WORKLOADS["decode_bf16_h32_s131072_peaked"].make()
+
+
+SAMPLED_HEADS = [0, 5, 13, 22, 31]
+
+
+def test_workload_bf16_h32_s131072_peaked(device, long_peaked):
+    """Full size, the launch the benchmark times; sampled heads against the oracle,
+    every head checked for finiteness."""
+    d = long_peaked
+    announce("decode_bf16_h32_s131072_peaked")
+    o = run_single(d, device)
+    assert torch.isfinite(o.float()).all()
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=SAMPLED_HEADS)
+    assert_close(o[SAMPLED_HEADS], ref, "bf16", "s131072 sampled heads")
+
+
+def test_partials_of_long_peaked(device, long_peaked):
+    """The split kernel alone: the workspace partials (normalised O_s, natural-log lse_s)
+    against the oracle's per-split definition, for two heads."""
+    d = long_peaked
+    plan = fd.decode_plan(32, 32, d["S"], "bf16")
+    assert plan["merge"] == 1
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=device)
+    announce(f"s131072 partials chunk {plan['chunk']} splits {plan['num_splits']}")
+    run_single(d, device, ws=ws)
+    ws_o, ws_lse = fd.workspace_views(ws, plan, 1, 32)
+    for h in (3, 27):
+        O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], plan["chunk"], heads=[h])
+        assert_close(ws_o[0, h], O_s[0], "bf16", f"partials head {h}")
+        np.testing.assert_allclose(ws_lse[0, h].cpu().numpy(), lse_s[0], rtol=1e-5, atol=5e-4)
+
+
+def _sample_pairs(B, H, lens, n, seed):
+    rng = np.random.default_rng(seed)
+    order = np.argsort(lens)
+    bs = sorted(set([int(order[0]), int(order[-1])] + rng.choice(B, size=n, replace=False).tolist()))
+    return [(b, int(h)) for b in bs for h in rng.choice(H, size=3, replace=False)]
+
+
+@pytest.mark.parametrize("name", ["paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"])
+def test_paged_workloads(name, device):
+    w = inputs.WORKLOADS[name]
+    announce(f"{name} (generating inputs)")
+    d = w.make()
+    announce(f"{name} run")
+    o = run_paged(d, device)
+    assert torch.isfinite(o.float()).all()
+    pairs = _sample_pairs(w.B, w.H, d["seq_lens"].numpy(), 6, 3)
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           d["page_size"], d["scale"], pairs=pairs)
+    got = torch.stack([o[b, h] for b, h in pairs])
+    assert_close(got, ref, w.dtype, name)
+
+
+# ------------------------------------------------------------------ invariance and tails
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_split_count_and_chunk_invariance(dtype, device):
+    d = inputs.single_inputs(8, 8, 4099, 128, dtype, 51, peak_frac=0.01)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    for opt in [fd.options(force_num_splits=n) for n in (1, 2, 3, 7, 64)] + [None] + \
+               [fd.options(force_chunk=c) for c in (64, 192, 1024)]:
+        plan = fd.decode_plan(8, 8, 4099, dtype, 0, opt)
+        announce(f"invariance {dtype} chunk {plan['chunk']} splits {plan['num_splits']}")
+        o = run_single(d, device, opt=opt)
+        assert_close(o, ref, dtype, f"chunk {plan['chunk']}")
+
+
+@pytest.mark.parametrize("S", [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 257, 1000, 4097])
+def test_ragged_lengths(S, device):
+    announce(f"ragged S={S}")
+    d = inputs.single_inputs(4, 2, S, 128, "bf16", 60 + S)
+    for opt in (None, fd.options(force_chunk=64)):
+        o = run_single(d, device, opt=opt)
+        ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+        assert_close(o, ref, "bf16", f"S={S}")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 4), (16, 4), (16, 2), (12, 4), (12, 2), (7, 1), (32, 4)])
+def test_head_groups(H, Hkv, device):
+    """Group sizes 1, 2, 4, 8, 3, 6, 7: each q head reads KV head h // (H / Hkv)."""
+    announce(f"heads H={H} Hkv={Hkv}")
+    d = inputs.single_inputs(H, Hkv, 700, 128, "bf16", 70 + H * 10 + Hkv)
+    o = run_single(d, device, opt=fd.options(force_chunk=256))
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    assert_close(o, ref, "bf16", f"H={H} Hkv={Hkv}")
+
+
+# ------------------------------------------------------------------ paged addressing
+
+
+def _pools(lens, Hkv, ps, dtype, seed):
+    """The same tokens stored (a) in order with an identity table and (b) on shuffled
+    pages, every slot past L_b and three spare pages filled with NaN."""
+    B = len(lens)
+    rng = np.random.default_rng(seed)
+    counts = [-(-L // ps) for L in lens]
+    P = sum(counts)
+    perm = rng.permutation(P)
+    nan_pool = torch.full((P + 3, ps, Hkv, 128), float("nan"), dtype=DT[dtype])
+    kA, vA, kB, vB = nan_pool.clone(), nan_pool.clone(), nan_pool.clone(), nan_pool.clone()
+    tA = torch.full((B, max(counts)), -1, dtype=torch.int32)
+    tB = tA.clone()
+    nxt = 0
+    for b, L in enumerate(lens):
+        kt = inputs.normal(np.random.SeedSequence([seed, b, 0]), (L, Hkv, 128), dtype)
+        vt = inputs.normal(np.random.SeedSequence([seed, b, 1]), (L, Hkv, 128), dtype)
+        for j in range(counts[b]):
+            n = min(ps, L - j * ps)
+            tA[b, j] = nxt
+            tB[b, j] = int(perm[nxt])
+            kA[nxt, :n] = kt[j * ps:j * ps + n]
+            vA[nxt, :n] = vt[j * ps:j * ps + n]
+            kB[int(perm[nxt]), :n] = kt[j * ps:j * ps + n]
+            vB[int(perm[nxt]), :n] = vt[j * ps:j * ps + n]
+            nxt += 1
+    return kA, vA, tA, kB, vB, tB
+
+
+@pytest.mark.parametrize("ps", [1, 16, 64, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_paged_addressing_is_bit_exact(ps, dtype, device):
+    """Shuffled table over a scattered pool == identity table over in-order pages, bit
+    for bit; NaN in tail slots and unreferenced pages never reaches the output. Lengths
+    {1, 17, 1000, 4096} are those of the paged GQA harness on "FlashAttention 与推理算子"."""
+    lens = [1, 17, 1000, 4096]
+    B, H, Hkv = 4, 32, 8
+    kA, vA, tA, kB, vB, tB = _pools(lens, Hkv, ps, dtype, 80 + ps)
+    q = inputs.normal(np.random.SeedSequence(81), (B, H, 128), dtype)
+    L = torch.tensor(lens, dtype=torch.int32)
+    scale = inputs.default_scale(128)
+    outs = []
+    for kc, vc, t in ((kA, vA, tA), (kB, vB, tB)):
+        announce(f"paged bit-exact ps={ps} {dtype}")
+        o = fd.fd_paged_decode(q.to(device), kc.to(device), vc.to(device), t.to(device), L.to(device), ps,
+                               scale=scale, max_seq_len=max(lens), total_kv=sum(lens),
+                               opt=fd.options(force_chunk=512))
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.isfinite(outs[0].float()).all()
+    assert torch.equal(outs[0], outs[1])
+    ref, _ = oracle.paged_decode_attention(q, kB, vB, tB, L, ps, scale)
+    assert_close(outs[1], ref, dtype, f"paged ps={ps}")
+
+
+def test_paged_empty_and_clamped_sequences(device):
+    """L_b = 0 gives zeros; the rest of the batch is unaffected."""
+    lens = [0, 5, 0, 300]
+    d = inputs.paged_inputs(4, 8, 2, 128, "bf16", 16, lens, 90)
+    announce("paged empty sequences")
+    for opt in (None, fd.options(force_chunk=64)):
+        o = run_paged(d, device, opt=opt)
+        assert torch.equal(o[0].cpu(), torch.zeros(8, 128, dtype=torch.bfloat16))
+        assert torch.equal(o[2].cpu(), torch.zeros(8, 128, dtype=torch.bfloat16))
+        ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                               d["seq_lens"], 16, d["scale"])
+        assert_close(o, ref, "bf16", "paged with empty sequences")
+
+
+def test_paged_split_invariance(device):
+    lens = [4097, 1, 3000, 64, 8191]
+    d = inputs.paged_inputs(5, 16, 2, 128, "f16", 16, lens, 91)
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"])
+    for opt in (None, fd.options(force_chunk=64), fd.options(force_chunk=1024), fd.options(force_num_splits=3)):
+        plan = fd.paged_plan(5, 16, 2, "f16", 16, max(lens), sum(lens), 0, opt)
+        announce(f"paged invariance chunk {plan['chunk']}")
+        o = run_paged(d, device, opt=opt)
+        assert_close(o, ref, "f16", f"paged chunk {plan['chunk']}")
+
+
+def test_workspace_too_small_is_rejected(device):
+    d = to_dev(inputs.single_inputs(8, 8, 4096, 128, "bf16", 95), device)
+    plan = fd.decode_plan(8, 8, 4096, "bf16", 0, fd.options(force_num_splits=4))
+    ws = torch.empty(plan["workspace_bytes"] - 4, dtype=torch.uint8, device=device)
+    with pytest.raises(fd.FdError) as e:
+        fd.fd_decode(d["q"], d["k"], d["v"], scale=0.1, ws=ws, opt=fd.options(force_num_splits=4))
+    assert e.value.name == "FD_ERR_WORKSPACE"
