@@ -64,7 +64,7 @@ def load_traffic(workload: str) -> dict | None:
 class Case:
     """A workload placed in device memory with rotated KV copies and its C-ABI arguments."""
 
-    def __init__(self, w, chunk: int = 0):
+    def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None):
         import torch
 
         import decode_attention_13_amd as fd
@@ -74,10 +74,12 @@ class Case:
         self.fd = fd
         self.lib = fd.lib()
         dev = torch.device("cuda:0")
-        log(f"generating {w.name}")
-        d = w.make()
+        if data is None:
+            log(f"generating {w.name}")
+            data = w.make()
+        d = data
         self.d = d
-        self.opt = fd.options(force_chunk=chunk) if chunk else None
+        self.opt = fd.options(force_chunk=chunk, kernel=kernel) if (chunk or kernel != "auto") else None
         esize = torch.tensor([], dtype=inputs_dtype(w.dtype)).element_size()
         self.dtype_code = binding.FD_DTYPE[inputs_dtype(w.dtype)]
         if w.kind == "single":
@@ -150,6 +152,7 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
     base = case.opt
     opts = [case.fd.options(force_num_splits=base.force_num_splits if base else 0,
                             force_chunk=base.force_chunk if base else 0,
+                            kernel=base.force_kernel if base else 0,
                             split_begin_event=begins[i], split_end_event=ends[i]) for i in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -220,6 +223,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--chunk", type=int, default=0, help="force tokens per split (multiple of 64)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"], help="force the split kernel")
     ap.add_argument("--sweep", action="store_true", help="also time the pages' KV-length sweep (4k..128k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
@@ -240,7 +244,7 @@ def main() -> int:
 
     from decode_attention_13_amd.inputs import WORKLOADS, sweep_workload
     w = WORKLOADS[args.workload]
-    case = Case(w, args.chunk)
+    case = Case(w, args.chunk, args.kernel)
     t = time_steps(case, args.steps, args.warmup)
     step_s = t["wall_s"]
     split_s = t["split_mean_s"]

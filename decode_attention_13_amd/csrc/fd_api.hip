@@ -43,26 +43,44 @@ long long pow2_floor(long long x) {
     return p;
 }
 
-// Planner constants.
-//  - Workgroups aimed at per compute unit: a split-kernel workgroup is 4 waves
-//    whose register double buffer keeps 8 KB of K/V in flight per wave, so a
-//    few resident workgroups per CU keep the HBM queues full; enough of them
-//    also leave room for the sequence-length tail.
+// Planner constants (measured on MI355X, see the tuning notes of the design).
+//  - Workgroups aimed at per compute unit: a split-kernel workgroup is 4 waves,
+//    each with one or two tiles of K/V in flight, so a few resident workgroups
+//    per CU keep the HBM queues full. A paged batch has ragged lengths, so it
+//    is cut finer: small splits spread long sequences over the whole chip.
 //  - Chunk bounds: long enough to amortise a workgroup's start (q load, first
 //    round trip to HBM) and its partial write, short enough to spread short
 //    caches over the chip.
 constexpr int kTargetWgsPerCu = 4;
-constexpr int kMinChunk = 256;
+constexpr int kTargetWgsPerCuPaged = 16;
+constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 16384;
 constexpr int kMaxSplits = 4096;
 
 std::mutex g_cu_mutex;
 std::vector<int> g_cu_cache;
 
-int pick_heads_per_group(int G) {
+// Heads per workgroup of the vector-ALU kernel: the largest compiled group
+// size dividing G (a workgroup reads its KV rows once for all its heads).
+int valu_heads_per_group(int G) {
     for (int gt : {8, 4, 2, 1})
         if (G % gt == 0) return gt;
     return 1;
+}
+
+// The matrix-core kernel takes up to 16 heads (one MFMA tile of columns).
+int mfma_heads_per_group(int G) {
+    if (G <= 16) return G;
+    return G % 16 == 0 ? 16 : 0;
+}
+
+// Matrix cores when a group of query heads forms a tile (16-bit inputs, >= 3
+// heads per KV head); the vector ALUs otherwise.
+int pick_kernel(fd_dtype dtype, int G, int forced) {
+    const bool mfma_ok = dtype != FD_DTYPE_F32 && mfma_heads_per_group(G) > 0;
+    if (forced == FD_KERNEL_VALU) return FD_KERNEL_VALU;
+    if (forced == FD_KERNEL_MFMA) return mfma_ok ? FD_KERNEL_MFMA : -1;
+    return (mfma_ok && G >= 3) ? FD_KERNEL_MFMA : FD_KERNEL_VALU;
 }
 
 fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_options *opt) {
@@ -88,12 +106,11 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
 // lengths (one sequence for contiguous decode), `page_size` 0 when contiguous.
 fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long long total, int page_size,
                     int num_cus, const fd_options *opt, fd_plan *p) {
-    (void)dtype;
     const int G = H / Hkv;
-    const int force_kernel = opt ? opt->force_kernel : FD_KERNEL_AUTO;
-    if (force_kernel == FD_KERNEL_MFMA)
-        return fail(FD_ERR_UNSUPPORTED, "the matrix-core split kernel is not available in this build");
-    const int gt = pick_heads_per_group(G);
+    const int kernel = pick_kernel(dtype, G, opt ? opt->force_kernel : FD_KERNEL_AUTO);
+    if (kernel < 0)
+        return fail(FD_ERR_UNSUPPORTED, "the matrix-core kernel needs f16/bf16 and H/Hkv <= 16 or a multiple of 16");
+    const int gt = kernel == FD_KERNEL_MFMA ? mfma_heads_per_group(G) : valu_heads_per_group(G);
     const long long slices = (long long)Hkv * (G / gt);
 
     long long chunk;
@@ -106,7 +123,7 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
         const long long work = std::max(total, 1LL) * slices;
-        const long long target = (long long)num_cus * kTargetWgsPerCu;
+        const long long target = (long long)num_cus * (page_size > 0 ? kTargetWgsPerCuPaged : kTargetWgsPerCu);
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
@@ -129,12 +146,15 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     }
 
     std::memset(p, 0, sizeof(*p));
-    p->kernel = FD_KERNEL_VALU;
+    p->kernel = kernel;
     p->heads_per_group = gt;
     p->chunk = (int)chunk;
     p->num_splits = (int)splits;
-    p->grid_x = (int)splits;
-    p->grid_y = (int)slices;
+    // Head slices vary fastest: workgroups go to the XCDs round-robin by linear
+    // id, so this spreads every split index (and the empty tail splits of short
+    // sequences) evenly over the XCDs.
+    p->grid_x = (int)slices;
+    p->grid_y = (int)splits;
     p->grid_z = B;
     p->threads = 256;
     p->merge = splits > 1 ? 1 : 0;
@@ -179,7 +199,12 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_begin_event), stream) != hipSuccess)
             return fail(FD_ERR_LAUNCH, "hipEventRecord(split_begin_event) failed");
     }
-    hipError_t e = fd::launch_split_valu(dtype, plan.heads_per_group, paged, shape, a, stream);
+    a.heads_per_wg = plan.heads_per_group;
+    // 16-token blocks stay inside one page when pages hold at least 16 tokens.
+    const int mode = !paged ? fd::kContig : ((1 << a.page_shift) >= 16 ? fd::kPagedBlock : fd::kPagedRow);
+    hipError_t e = plan.kernel == FD_KERNEL_MFMA
+                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, shape, a, stream)
+                       : fd::launch_split_valu(dtype, plan.heads_per_group, mode, shape, a, stream);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
     if (opt && opt->split_end_event) {
         if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_end_event), stream) != hipSuccess)

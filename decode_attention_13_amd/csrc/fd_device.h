@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fd_internal.h"
+
 namespace fd {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -158,6 +160,52 @@ struct Elem<_Float16> {
     }
     __device__ static _Float16 store_cast(float x) { return (_Float16)x; }  // round to nearest even
 };
+
+// ---------------------------------------------------------------- KV addressing
+// Where the row of (token t, KV head kvh) lives, in bytes from the cache base:
+//   contiguous [S, Hkv, D]:                 (t*Hkv + kvh) * row
+//   paged [pages, page_size, Hkv, D]:       ((page(t)*page_size + t%page_size)*Hkv + kvh) * row
+// with page(t) = block_table[b][t / page_size] ("FlashAttention 与推理算子",
+// section "PagedAttention") and row = D * sizeof(T).
+// Kernels walk tokens in 16-token blocks starting at multiples of 16. When the
+// cache is contiguous, or paged with page_size >= 16, a block lies inside one
+// page, so its base is the same for every lane (held in scalar registers) and
+// a lane adds the 32-bit offset (t - block start) * Hkv * row. With smaller
+// pages every row is looked up on its own.
+template <int MODE>
+struct KvAddr {
+    const int *pages;       // LDS: the split's slice of the block table (paged)
+    int page_first;         // table index of pages[0]
+    int page_shift;
+    int token_bytes;        // Hkv * row: distance between consecutive slots/tokens
+    size_t head_bytes;      // kvh * row
+
+    // Byte offset of the first row of the 16-token block starting at T.
+    __device__ size_t block(int T) const {
+        if constexpr (MODE == kContig) {
+            return (size_t)T * token_bytes + head_bytes;
+        } else {
+            const int page = __builtin_amdgcn_readfirstlane(pages[(T >> page_shift) - page_first]);
+            const size_t slot_row = ((size_t)page << page_shift) + (size_t)(T & ((1 << page_shift) - 1));
+            return slot_row * token_bytes + head_bytes;
+        }
+    }
+    // Byte offset of any single row (every mode).
+    __device__ size_t row(int t) const {
+        if constexpr (MODE == kContig) {
+            return (size_t)t * token_bytes + head_bytes;
+        } else {
+            const int page = pages[(t >> page_shift) - page_first];
+            const size_t slot_row = ((size_t)page << page_shift) + (size_t)(t & ((1 << page_shift) - 1));
+            return slot_row * token_bytes + head_bytes;
+        }
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ uint4 load_stream16_at(const T *base, size_t byte_off) {
+    return load_stream16(reinterpret_cast<const char *>(base) + byte_off);
+}
 
 // ---------------------------------------------------------------- softmax state
 // Online-softmax state in the log2 domain: running max m (of scale*log2(e)*s),

@@ -17,6 +17,9 @@ constexpr int kMaxSplitPages = 1024;
 
 constexpr float kLog2eHost = 1.4426950408889634f;  // log2(e), folded into the scale on the host
 
+// How a split kernel addresses K/V rows (see KvAddr in fd_device.h).
+enum AddrMode { kContig = 0, kPagedBlock = 1, kPagedRow = 2 };
+
 struct SplitArgs {
     const void *q;          // [B, H, D]
     const void *k;          // contiguous [S, Hkv, D] or cache [num_pages, page_size, Hkv, D]
@@ -27,6 +30,7 @@ struct SplitArgs {
     float *ws_lse;          // [B, H, num_splits]
     void *out;              // [B, H, D] (direct mode)
     int H, Hkv, G;          // G = H / Hkv
+    int heads_per_wg;       // query heads of one KV head computed by one workgroup
     int max_len;            // contiguous: S; paged: clamp bound for seq_lens
     int chunk;              // tokens per split
     int num_splits;
@@ -53,10 +57,11 @@ struct LaunchShape {
     dim3 block;
 };
 
-// Each returns hipSuccess or the launch error. `gt` = heads per workgroup.
-hipError_t launch_split_valu(fd_dtype dtype, int gt, bool paged, const LaunchShape &shape, const SplitArgs &a,
+// Each returns hipSuccess or the launch error. `gt` = heads per workgroup,
+// `mode` = AddrMode of fd_device.h (contiguous, paged by 16-token block, paged by row).
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
                              hipStream_t stream);
-hipError_t launch_split_mfma(fd_dtype dtype, int gt, bool paged, const LaunchShape &shape, const SplitArgs &a,
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
                              hipStream_t stream);
 hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, hipStream_t stream);
 

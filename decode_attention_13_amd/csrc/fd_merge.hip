@@ -51,31 +51,31 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     mx = wave_max(mx);
     const float mu = finite_or_zero(mx);
 
+    // Splits in groups of 64: lane i computes split (s0 + i)'s weight, the
+    // weights reach every lane through readlane, and each lane accumulates its
+    // two output elements with 8 independent loads in flight.
     const float2 *src = reinterpret_cast<const float2 *>(a.ws_o + row0 * kHeadDim) + lane;
-    float o0 = 0.f, o1 = 0.f, wsum = 0.f;
-    int s = 0;
-    for (; s + 4 <= n; s += 4) {
-        float w[4];
-        float2 x[4];
+    float o0 = 0.f, o1 = 0.f, wpart = 0.f;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int cnt = min(64, n - s0);
+        const float w = lane < cnt ? exp2_fast((lse[s0 + lane] - mu) * kLog2e) : 0.f;
+        wpart += w;
+        for (int i = 0; i < cnt; i += 8) {
+            float2 x[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = exp2_fast((lse[s + i] - mu) * kLog2e);
-            x[i] = src[(size_t)(s + i) * (kHeadDim / 2)];
-        }
+            for (int u = 0; u < 8; ++u)
+                if (i + u < cnt) x[u] = src[(size_t)(s0 + i + u) * (kHeadDim / 2)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wsum += w[i];
-            o0 = __builtin_fmaf(w[i], x[i].x, o0);
-            o1 = __builtin_fmaf(w[i], x[i].y, o1);
+            for (int u = 0; u < 8; ++u) {
+                if (i + u < cnt) {
+                    const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i + u));
+                    o0 = __builtin_fmaf(wu, x[u].x, o0);
+                    o1 = __builtin_fmaf(wu, x[u].y, o1);
+                }
+            }
         }
     }
-    for (; s < n; ++s) {
-        const float w = exp2_fast((lse[s] - mu) * kLog2e);
-        const float2 x = src[(size_t)s * (kHeadDim / 2)];
-        wsum += w;
-        o0 = __builtin_fmaf(w, x.x, o0);
-        o1 = __builtin_fmaf(w, x.y, o1);
-    }
+    const float wsum = wave_sum(wpart);
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     typedef typename Pair<T>::type P2;
     P2 *out = reinterpret_cast<P2 *>(reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h) * kHeadDim) + lane;

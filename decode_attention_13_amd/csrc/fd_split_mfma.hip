@@ -1,0 +1,357 @@
+// fd_split_mfma.hip -- split kernel on the matrix cores for grouped-query heads
+// (gfx950, wave64, v_mfma_f32_16x16x32_{bf16,f16}).
+//
+// When G query heads share one KV head, one workgroup reads each K/V row once
+// and serves all G heads ("FlashAttention 与推理算子", exercise 3: one block per
+// (sequence, KV head) computing every query head of the group). With G >= 4
+// the per-row work (G dot products and G axpys over 128 elements) is a real
+// matrix tile, so it runs on MFMA; G is padded to the 16 columns of the tile.
+//
+// Per wave and tile of 32 tokens:
+//   S^T[token, head] = K[token, :] . Q[head, :]    two 16x16x32 MFMA chains of 4
+//       A = K rows straight from 16-byte global loads (lane: token = lane%16,
+//       head-dim slot group lane/16), B = Q (loaded once).
+//   online softmax per head (column) in the log2 domain, fp32;
+//   O^T[d, head] += V^T[d, token] . P[token, head]  eight 16x16x32 MFMAs
+//       B = P converted to the input type, taken from the S accumulators with
+//       no lane movement: token slot (lane/16)*8 + j holds token
+//       (j/4)*16 + (lane/16)*4 + j%4, exactly the tokens the S accumulator of
+//       that lane holds. A = V^T, read from a padded LDS copy of the V tile with
+//       ds_read_b64_tr_b16 (within 16 lanes: source lane 4e+b supplies 4
+//       elements of row e; result lane c receives column c of rows 0..3).
+// The contraction order inside an MFMA is free, so the head-dim slot order of
+// K and Q only has to agree with itself; it is chosen so that the four lanes
+// of a row load 64 contiguous bytes per instruction.
+//
+// The wave's next tile of K and V is loaded into registers while the current
+// one is computed. The four waves' states are merged once at the end through
+// LDS.
+#include "fd_device.h"
+#include "fd_internal.h"
+
+namespace fd {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTile = 32;                // tokens per wave tile
+constexpr int kRowPad = 288;             // LDS bytes per V row: 256 + 32 keeps 8 rows on disjoint banks
+constexpr int kVRegion = kTile * kRowPad;  // LDS bytes per wave
+constexpr int kMaxHeads = 16;            // MFMA tile columns
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+    __device__ static uint32_t pack2(float x, float y) {  // round to nearest even
+        return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
+    }
+    __device__ static float lo_of(uint32_t w) { return bf16_lo(w); }
+    __device__ static float hi_of(uint32_t w) { return bf16_hi(w); }
+};
+
+template <>
+struct Mfma<_Float16> {
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+    __device__ static uint32_t pack2(float x, float y) {
+        return __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
+    }
+    __device__ static float lo_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
+    __device__ static float hi_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+};
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
+    constexpr bool PAGED = MODE != kContig;
+    using M = Mfma<T>;
+    using E = Elem<T>;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;   // 16-lane group
+    const int c = lane & 15;   // row/column inside the 16x16 tile
+    const int split = blockIdx.y;
+    const int G = a.G;
+    const int slices = G / a.heads_per_wg;
+    const int kvh = blockIdx.x / slices;
+    const int h0 = kvh * G + (blockIdx.x - kvh * slices) * a.heads_per_wg;
+    const int nh = a.heads_per_wg;  // heads of this workgroup (<= 16)
+    const int b = blockIdx.z;
+
+    __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
+    __shared__ __attribute__((aligned(16))) char s_buf[kWaves * kVRegion];
+    __shared__ float s_m[kWaves][kMaxHeads];
+    __shared__ float s_l[kWaves][kMaxHeads];
+
+    int L = a.max_len;
+    if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
+    const int t_begin = split * a.chunk;
+    if (t_begin >= L) {
+        if (a.direct && split == 0) {
+            T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
+            for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
+        }
+        return;
+    }
+    const int t_end = min(t_begin + a.chunk, L);
+
+    int page_first = 0;
+    if (PAGED) {
+        page_first = t_begin >> a.page_shift;
+        const int n_pages = ((t_end - 1) >> a.page_shift) - page_first + 1;
+        const int32_t *row = a.block_table + (size_t)b * a.max_blocks + page_first;
+        for (int i = threadIdx.x; i < n_pages; i += kThreads) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
+        __syncthreads();
+    }
+    const T *kbase = reinterpret_cast<const T *>(a.k);
+    const T *vbase = reinterpret_cast<const T *>(a.v);
+    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(T),
+                   (size_t)kvh * kHeadDim * sizeof(T)};
+
+    // B operand of S: q[h0 + c][kk*32 + g*8 .. +8], zero for padded heads.
+    uint4 qb[4];
+    {
+        const T *qrow = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.H + h0 + min(c, nh - 1)) * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            qb[kk] = load16(qrow + kk * 32 + g * 8);
+            if (c >= nh) qb[kk] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;  // running max of head c (same in the 4 lane groups)
+    float lsum = 0.f;     // this lane's share of the running sum of head c
+
+    // LDS pointer of this wave's V region (the low 32 bits of a generic LDS
+    // address are its LDS offset).
+    lds_char *vreg = (lds_char *)(uintptr_t)(s_buf + wave * kVRegion);
+    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+
+    // A tile is two 16-token blocks. When the second block holds no valid token
+    // its rows are clamped into the first, so both are addressed from block 0.
+    auto block_start = [&](int t0, int h) { return (h == 0 || t0 + 16 < t_end) ? t0 + 16 * h : t0; };
+    auto load_k = [&](int j, uint4 (&kx)[2][4]) {
+        const int t0 = t_begin + j * kTile;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int tok = min(t0 + sb * 16 + c, t_end - 1);
+            if constexpr (MODE == kPagedRow) {
+                const size_t off = A.row(tok) + (size_t)g * 16;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kx[sb][kk] = load16(reinterpret_cast<const char *>(kbase) + off + kk * 64);
+            } else {
+                const int B = block_start(t0, sb);
+                const T *kb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(kbase) + A.block(B));
+                const uint32_t off = (uint32_t)(tok - B) * (uint32_t)A.token_bytes + g * 16;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kx[sb][kk] = load16(reinterpret_cast<const char *>(kb) + off + kk * 64);
+            }
+        }
+    };
+    auto load_v = [&](int j, uint4 (&vx)[8]) {
+        const int t0 = t_begin + j * kTile;
+        size_t base[2] = {0, 0};
+        if constexpr (MODE != kPagedRow) {
+            base[0] = A.block(block_start(t0, 0));
+            base[1] = A.block(block_start(t0, 1));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tok = min(t0 + 4 * i + g, t_end - 1);
+            if constexpr (MODE == kPagedRow) {
+                vx[i] = load_stream16_at(vbase, A.row(tok) + c * 16);
+            } else {
+                const int h = i >> 2;
+                const T *vb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(vbase) + base[h]);
+                vx[i] = load_stream16_at(vb, (uint32_t)(tok - block_start(t0, h)) * (uint32_t)A.token_bytes + c * 16);
+            }
+        }
+    };
+
+    // K: one register set, refilled with the wave's next tile as soon as the S
+    // MFMAs have consumed it. V: two register sets used as a ring, so the V rows
+    // of the next two tiles are in flight while this tile is computed.
+    uint4 kx[2][4], vA[8], vB[8];
+    auto tile = [&](int j, uint4 (&vcur)[8]) {
+        const int t0 = t_begin + j * kTile;
+        // V tile -> LDS (row r = token t0 + r, padded rows), then refill the set
+        // with the tile after next.
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *(lds_u32x4 *)(vreg + (4 * i + g) * kRowPad + c * 16) = u32x4{vcur[i].x, vcur[i].y, vcur[i].z, vcur[i].w};
+        if (j + 2 * kWaves < ntiles) load_v(j + 2 * kWaves, vcur);
+        // S^T tiles: s[sb][i] = score of token t0 + sb*16 + g*4 + i for head c
+        f32x4 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) s[sb] = M::mma(kx[sb][kk], qb[kk], s[sb]);
+        }
+        if (j + kWaves < ntiles) load_k(j + kWaves, kx);
+        float x[8];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = t0 + sb * 16 + g * 4 + i < t_end;
+                x[sb * 4 + i] = valid ? s[sb][i] * a.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, x[sb * 4 + i]);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m, mt);
+        const float mu = finite_or_zero(m_new);
+        const float alpha = exp2_fast(m - mu);
+        m = m_new;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = exp2_fast(x[e] - mu);
+            ps += p[e];
+        }
+        lsum = lsum * alpha + ps;
+        // P in two 16-bit parts, p = hi + lo (+ 2^-16 p): two MFMAs per block
+        // keep P.V close to fp32 precision.
+        uint4 ph, pl;
+        {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                hw[e2] = M::pack2(p[2 * e2], p[2 * e2 + 1]);
+                const float h0v = M::lo_of(hw[e2]), h1v = M::hi_of(hw[e2]);
+                lw[e2] = M::pack2(p[2 * e2] - h0v, p[2 * e2 + 1] - h1v);
+            }
+            ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        // Rescale only when some head's running max moved (alpha == 1 is exact).
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+        }
+        // O^T[d, head] += V^T[d, token slot] . P[token slot, head]
+        const int e = c >> 2, bq = c & 3;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int col_bytes = (db * 16 + bq * 4) * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<lds_i16x4 *>(vreg + (g * 4 + e) * kRowPad + col_bytes));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<lds_i16x4 *>(vreg + (16 + g * 4 + e) * kRowPad + col_bytes));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+            const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+            acc[db] = M::mma(va, ph, acc[db]);
+            acc[db] = M::mma(va, pl, acc[db]);
+        }
+    };
+    int j = wave;
+    if (j < ntiles) {
+        load_k(j, kx);
+        load_v(j, vA);
+        if (j + kWaves < ntiles) load_v(j + kWaves, vB);
+    }
+    while (j < ntiles) {
+        tile(j, vA);
+        j += kWaves;
+        if (j >= ntiles) break;
+        tile(j, vB);
+        j += kWaves;
+    }
+
+    // Head c's running sum over the wave: the four lane groups hold disjoint tokens.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    __syncthreads();  // every wave is done with its V region; reuse it for the merge
+    float *s_acc = reinterpret_cast<float *>(s_buf);  // [wave][head][d]
+    if (c < nh) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<f32x4 *>(&s_acc[(wave * kMaxHeads + c) * kHeadDim + db * 16 + g * 4]) = acc[db];
+        if (g == 0) {
+            s_m[wave][c] = m;
+            s_l[wave][c] = lsum;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) {
+        const int hh = i / kHeadDim;
+        const int d = i - hh * kHeadDim;
+        float Mx = s_m[0][hh];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][hh]);
+        const float mu = finite_or_zero(Mx);
+        float l = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wgt = exp2_fast(s_m[w][hh] - mu);
+            l = __builtin_fmaf(wgt, s_l[w][hh], l);
+            o = __builtin_fmaf(wgt, s_acc[(w * kMaxHeads + hh) * kHeadDim + d], o);
+        }
+        const float out = o / l;
+        const size_t bh = (size_t)b * a.H + h0 + hh;
+        if (a.direct) {
+            reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = E::store_cast(out);
+        } else {
+            const size_t row = bh * a.num_splits + split;
+            a.ws_o[row * kHeadDim + d] = out;
+            if (d == 0) a.ws_lse[row] = (Mx + log2_fast(l)) * kLn2;
+        }
+    }
+}
+
+template <typename T, int MODE>
+hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+    SplitArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&split_mfma_kernel<T, MODE>), s.grid, s.block, args, 0, st);
+}
+
+template <typename T>
+hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+    switch (mode) {
+        case kContig: return launch_one<T, kContig>(s, a, st);
+        case kPagedBlock: return launch_one<T, kPagedBlock>(s, a, st);
+        case kPagedRow: return launch_one<T, kPagedRow>(s, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
+                             hipStream_t st) {
+    if (gt < 1 || gt > kMaxHeads) return hipErrorInvalidValue;
+    switch (dtype) {
+        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, s, a, st);
+        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, s, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fd

@@ -31,18 +31,19 @@ constexpr int kRows = 4;               // rows per 16-lane group per wave tile
 constexpr int kWaveTile = 4 * kRows;   // tokens per wave tile
 constexpr int kWaves = kThreads / 64;
 
-template <typename T, int GT, bool PAGED>
+template <typename T, int GT, int MODE>
 __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
+    constexpr bool PAGED = MODE != kContig;
     using E = Elem<T>;
     constexpr int NL = E::kLoads;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;
     const int c = lane & 15;
-    const int split = blockIdx.x;
+    const int split = blockIdx.y;
     const int slices = a.G / GT;
-    const int kvh = blockIdx.y / slices;
-    const int h0 = kvh * a.G + (blockIdx.y - kvh * slices) * GT;
+    const int kvh = blockIdx.x / slices;
+    const int h0 = kvh * a.G + (blockIdx.x - kvh * slices) * GT;
     const int b = blockIdx.z;
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
@@ -73,16 +74,8 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 
     const T *kbase = reinterpret_cast<const T *>(a.k);
     const T *vbase = reinterpret_cast<const T *>(a.v);
-    const int page_mask = (1 << a.page_shift) - 1;
-    auto row_offset = [&](int t) -> size_t {  // element offset of (token t, KV head kvh, d = 0)
-        if constexpr (PAGED) {
-            const int page = s_pages[(t >> a.page_shift) - page_first];
-            const size_t slot_row = ((size_t)page << a.page_shift) + (size_t)(t & page_mask);
-            return (slot_row * a.Hkv + kvh) * kHeadDim;
-        } else {
-            return ((size_t)t * a.Hkv + kvh) * kHeadDim;
-        }
-    };
+    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(T),
+                   (size_t)kvh * kHeadDim * sizeof(T)};
 
     // q fragments of the GT heads: fp32 for fp32 inputs, packed pairs otherwise.
     float qf[GT][8];
@@ -114,15 +107,33 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 
     const int ntiles = (t_end - t_begin + kWaveTile - 1) / kWaveTile;
 
+    // Tile j covers the 16-aligned block [tb, tb + 16), tb = t_begin + 16 j; rows past
+    // t_end re-read the last valid row and are masked.
     auto load_tile = [&](int j, uint4 (&kx)[kRows][NL], uint4 (&vx)[kRows][NL]) {
-        const int t0 = t_begin + j * kWaveTile + grp * kRows;
+        const int tb = t_begin + j * kWaveTile;
+        const int t0 = tb + grp * kRows;
+        if constexpr (MODE == kPagedRow) {
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const size_t off = row_offset(min(t0 + r, t_end - 1));  // tail rows re-read a valid row, then masked
+            for (int r = 0; r < kRows; ++r) {
+                const size_t off = A.row(min(t0 + r, t_end - 1));
 #pragma unroll
-            for (int pc = 0; pc < NL; ++pc) {
-                kx[r][pc] = load_stream16(kbase + off + E::offset(c, pc));
-                vx[r][pc] = load_stream16(vbase + off + E::offset(c, pc));
+                for (int pc = 0; pc < NL; ++pc) {
+                    kx[r][pc] = load_stream16_at(kbase, off + E::offset(c, pc) * sizeof(T));
+                    vx[r][pc] = load_stream16_at(vbase, off + E::offset(c, pc) * sizeof(T));
+                }
+            }
+        } else {
+            const size_t base = A.block(tb);
+            const T *kb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(kbase) + base);
+            const T *vb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(vbase) + base);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const uint32_t off = (uint32_t)(min(t0 + r, t_end - 1) - tb) * (uint32_t)A.token_bytes;
+#pragma unroll
+                for (int pc = 0; pc < NL; ++pc) {
+                    kx[r][pc] = load_stream16_at(kb, off + E::offset(c, pc) * sizeof(T));
+                    vx[r][pc] = load_stream16_at(vb, off + E::offset(c, pc) * sizeof(T));
+                }
             }
         }
     };
@@ -242,35 +253,43 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     }
 }
 
-template <typename T, int GT, bool PAGED>
+template <typename T, int GT, int MODE>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, PAGED>), s.grid, s.block, args, 0,
+    return hipLaunchKernel(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, MODE>), s.grid, s.block, args, 0,
                            st);
 }
 
-template <typename T, bool PAGED>
+template <typename T, int MODE>
 hipError_t launch_gt(int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
     switch (gt) {
-        case 1: return launch_one<T, 1, PAGED>(s, a, st);
-        case 2: return launch_one<T, 2, PAGED>(s, a, st);
-        case 4: return launch_one<T, 4, PAGED>(s, a, st);
-        case 8: return launch_one<T, 8, PAGED>(s, a, st);
+        case 1: return launch_one<T, 1, MODE>(s, a, st);
+        case 2: return launch_one<T, 2, MODE>(s, a, st);
+        case 4: return launch_one<T, 4, MODE>(s, a, st);
+        case 8: return launch_one<T, 8, MODE>(s, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+    switch (mode) {
+        case kContig: return launch_gt<T, kContig>(gt, s, a, st);
+        case kPagedBlock: return launch_gt<T, kPagedBlock>(gt, s, a, st);
+        case kPagedRow: return launch_gt<T, kPagedRow>(gt, s, a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_split_valu(fd_dtype dtype, int gt, bool paged, const LaunchShape &s, const SplitArgs &a,
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
                              hipStream_t st) {
     switch (dtype) {
-        case FD_DTYPE_F32: return paged ? launch_gt<float, true>(gt, s, a, st) : launch_gt<float, false>(gt, s, a, st);
-        case FD_DTYPE_F16:
-            return paged ? launch_gt<_Float16, true>(gt, s, a, st) : launch_gt<_Float16, false>(gt, s, a, st);
-        case FD_DTYPE_BF16:
-            return paged ? launch_gt<__bf16, true>(gt, s, a, st) : launch_gt<__bf16, false>(gt, s, a, st);
+        case FD_DTYPE_F32: return launch_mode<float>(mode, gt, s, a, st);
+        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, gt, s, a, st);
+        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, gt, s, a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -81,8 +81,8 @@ typedef struct fd_plan {
     int kernel;          /* FD_KERNEL_VALU or FD_KERNEL_MFMA */
     int heads_per_group; /* query heads one workgroup computes (they share one KV head) */
     int chunk;           /* KV tokens per split */
-    int num_splits;      /* splits of the longest sequence = grid x */
-    int grid_x, grid_y, grid_z; /* split kernel grid: (splits, KV-head slices, sequences) */
+    int num_splits;      /* splits of the longest sequence = grid y */
+    int grid_x, grid_y, grid_z; /* split kernel grid: (KV-head slices, splits, sequences) */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: direct output */
     int reserved;

@@ -46,9 +46,9 @@ def test_status_strings():
 def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
     assert p["chunk"] % 64 == 0 and p["chunk"] >= 64
     assert p["num_splits"] == max(1, -(-max_len // p["chunk"]))
-    assert p["grid_x"] == p["num_splits"] and p["grid_z"] == B
+    assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
     gt = p["heads_per_group"]
-    assert (H // Hkv) % gt == 0 and p["grid_y"] == Hkv * (H // Hkv) // gt
+    assert (H // Hkv) % gt == 0 and p["grid_x"] == Hkv * (H // Hkv) // gt
     if p["merge"]:
         rows = B * H * p["num_splits"]
         assert p["ws_lse_offset"] >= rows * 128 * 4 and p["ws_lse_offset"] % 256 == 0

@@ -93,16 +93,19 @@ def test_worked_example(dtype, device):
     assert_close(o, ref, dtype, "worked example")
 
 
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_single_key_is_bit_exact(dtype, device):
-    """S = 1: p = 1, l = 1, so o must equal v_0 bit for bit (also through a paged table)."""
-    announce(f"single key {dtype}")
+def test_single_key_is_bit_exact(dtype, kernel, device):
+    """S = 1: p = 1, l = 1, so o must equal v_0 bit for bit (also through a paged table).
+    With 4 query heads per KV head, 16-bit inputs take the matrix-core kernel by default."""
+    announce(f"single key {dtype} {kernel}")
+    opt = fd.options(kernel=kernel)
     d = inputs.single_inputs(8, 2, 1, 128, dtype, 31)
-    o = run_single(d, device)
+    o = run_single(d, device, opt=opt)
     want = d["v"][0].repeat_interleave(4, dim=0)
     assert torch.equal(o.cpu(), want)
     p = inputs.paged_inputs(3, 8, 2, 128, dtype, 16, [1, 1, 1], 32)
-    o = run_paged(p, device)
+    o = run_paged(p, device, opt=opt)
     for b in range(3):
         page = int(p["block_table"][b, 0])
         assert torch.equal(o[b].cpu(), p["v_cache"][page, 0].repeat_interleave(4, dim=0))
@@ -183,52 +186,62 @@ def _sample_pairs(B, H, lens, n, seed):
 
 @pytest.mark.parametrize("name", ["paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"])
 def test_paged_workloads(name, device):
+    """Full size in the benchmark's launch (matrix-core kernel), then the vector-ALU
+    kernel forced; sampled (sequence, head) pairs against the oracle, including the
+    shortest and the longest sequence."""
     w = inputs.WORKLOADS[name]
     announce(f"{name} (generating inputs)")
     d = w.make()
-    announce(f"{name} run")
-    o = run_paged(d, device)
-    assert torch.isfinite(o.float()).all()
     pairs = _sample_pairs(w.B, w.H, d["seq_lens"].numpy(), 6, 3)
     ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
                                            d["page_size"], d["scale"], pairs=pairs)
-    got = torch.stack([o[b, h] for b, h in pairs])
-    assert_close(got, ref, w.dtype, name)
+    for kernel in ("auto", "valu"):
+        announce(f"{name} run {kernel}")
+        o = run_paged(d, device, opt=fd.options(kernel=kernel))
+        assert torch.isfinite(o.float()).all()
+        got = torch.stack([o[b, h] for b, h in pairs])
+        assert_close(got, ref, w.dtype, f"{name} {kernel}")
 
 
 # ------------------------------------------------------------------ invariance and tails
 
 
+@pytest.mark.parametrize("H,Hkv,kernel", [(8, 8, "auto"), (8, 8, "mfma"), (32, 4, "auto"), (32, 4, "valu")])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_split_count_and_chunk_invariance(dtype, device):
-    d = inputs.single_inputs(8, 8, 4099, 128, dtype, 51, peak_frac=0.01)
+def test_split_count_and_chunk_invariance(dtype, H, Hkv, kernel, device):
+    if dtype == "f32" and kernel == "mfma":
+        pytest.skip("the matrix-core kernel takes 16-bit inputs")
+    d = inputs.single_inputs(H, Hkv, 4099, 128, dtype, 51, peak_frac=0.01)
     ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
-    for opt in [fd.options(force_num_splits=n) for n in (1, 2, 3, 7, 64)] + [None] + \
-               [fd.options(force_chunk=c) for c in (64, 192, 1024)]:
-        plan = fd.decode_plan(8, 8, 4099, dtype, 0, opt)
-        announce(f"invariance {dtype} chunk {plan['chunk']} splits {plan['num_splits']}")
+    for n, c in [(1, 0), (2, 0), (3, 0), (7, 0), (64, 0), (0, 0), (0, 64), (0, 192), (0, 1024)]:
+        opt = fd.options(force_num_splits=n, force_chunk=c, kernel=kernel)
+        plan = fd.decode_plan(H, Hkv, 4099, dtype, 0, opt)
+        announce(f"invariance {dtype} H{H}/{Hkv} k{plan['kernel']} chunk {plan['chunk']} splits {plan['num_splits']}")
         o = run_single(d, device, opt=opt)
-        assert_close(o, ref, dtype, f"chunk {plan['chunk']}")
+        assert_close(o, ref, dtype, f"kernel {plan['kernel']} chunk {plan['chunk']}")
 
 
-@pytest.mark.parametrize("S", [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 257, 1000, 4097])
+@pytest.mark.parametrize("S", [0, 1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 255, 257, 1000, 4097])
 def test_ragged_lengths(S, device):
     announce(f"ragged S={S}")
-    d = inputs.single_inputs(4, 2, S, 128, "bf16", 60 + S)
-    for opt in (None, fd.options(force_chunk=64)):
+    d = inputs.single_inputs(8, 2, S, 128, "bf16", 60 + S)
+    for opt in (None, fd.options(force_chunk=64), fd.options(kernel="valu"),
+                fd.options(force_chunk=64, kernel="valu")):
         o = run_single(d, device, opt=opt)
         ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
         assert_close(o, ref, "bf16", f"S={S}")
 
 
-@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 4), (16, 4), (16, 2), (12, 4), (12, 2), (7, 1), (32, 4)])
-def test_head_groups(H, Hkv, device):
-    """Group sizes 1, 2, 4, 8, 3, 6, 7: each q head reads KV head h // (H / Hkv)."""
-    announce(f"heads H={H} Hkv={Hkv}")
+@pytest.mark.parametrize("kernel", ["auto", "valu", "mfma"])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 4), (16, 4), (16, 2), (12, 4), (12, 2), (7, 1), (32, 4),
+                                   (16, 1), (64, 2)])
+def test_head_groups(H, Hkv, kernel, device):
+    """Group sizes 1, 2, 4, 8, 3, 6, 7, 16, 32: each q head reads KV head h // (H / Hkv)."""
+    announce(f"heads H={H} Hkv={Hkv} {kernel}")
     d = inputs.single_inputs(H, Hkv, 700, 128, "bf16", 70 + H * 10 + Hkv)
-    o = run_single(d, device, opt=fd.options(force_chunk=256))
+    o = run_single(d, device, opt=fd.options(force_chunk=256, kernel=kernel))
     ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
-    assert_close(o, ref, "bf16", f"H={H} Hkv={Hkv}")
+    assert_close(o, ref, "bf16", f"H={H} Hkv={Hkv} {kernel}")
 
 
 # ------------------------------------------------------------------ paged addressing
@@ -262,9 +275,10 @@ def _pools(lens, Hkv, ps, dtype, seed):
     return kA, vA, tA, kB, vB, tB
 
 
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
 @pytest.mark.parametrize("ps", [1, 16, 64, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_paged_addressing_is_bit_exact(ps, dtype, device):
+def test_paged_addressing_is_bit_exact(ps, dtype, kernel, device):
     """Shuffled table over a scattered pool == identity table over in-order pages, bit
     for bit; NaN in tail slots and unreferenced pages never reaches the output. Lengths
     {1, 17, 1000, 4096} are those of the paged GQA harness on "FlashAttention 与推理算子"."""
@@ -276,10 +290,10 @@ def test_paged_addressing_is_bit_exact(ps, dtype, device):
     scale = inputs.default_scale(128)
     outs = []
     for kc, vc, t in ((kA, vA, tA), (kB, vB, tB)):
-        announce(f"paged bit-exact ps={ps} {dtype}")
+        announce(f"paged bit-exact ps={ps} {dtype} {kernel}")
         o = fd.fd_paged_decode(q.to(device), kc.to(device), vc.to(device), t.to(device), L.to(device), ps,
                                scale=scale, max_seq_len=max(lens), total_kv=sum(lens),
-                               opt=fd.options(force_chunk=512))
+                               opt=fd.options(force_chunk=512, kernel=kernel))
         torch.cuda.synchronize()
         outs.append(o.cpu())
     assert torch.isfinite(outs[0].float()).all()
