@@ -101,7 +101,7 @@ class Case:
         kd, vd = srcs[0].to(dev), srcs[1].to(dev)
         self.kv = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(self.copies - 1)]
         self.o = torch.empty_like(self.q)
-        self.ws = torch.empty(max(1, self.plan["workspace_bytes"]), dtype=torch.uint8, device=dev)
+        self.ws = fd.new_workspace(self.plan["workspace_bytes"], dev)
         self.stream = torch.cuda.current_stream()
         log(f"{w.name}: plan {self.plan}, {self.copies} KV copies of {self.kv_bytes / 1e6:.1f} MB")
 

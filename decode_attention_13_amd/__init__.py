@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     fd_decode,
     fd_paged_decode,
     lib,
+    new_workspace,
     options,
     paged_plan,
     workspace_views,

@@ -150,11 +150,16 @@ def _require(t: torch.Tensor, name: str, dtype=None) -> None:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """An uninitialised workspace of ``nbytes`` (uint8); it needs no initialisation."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def _workspace(ws, need: int, device) -> tuple[int, int, torch.Tensor | None]:
     if need == 0:
         return (ws.data_ptr() if ws is not None else 0), (ws.numel() * ws.element_size() if ws is not None else 0), None
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = new_workspace(need, device)
     return ws.data_ptr(), ws.numel() * ws.element_size(), ws
 
 

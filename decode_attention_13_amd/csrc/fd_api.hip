@@ -185,31 +185,23 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         if (!aligned16(ws)) return fail(FD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
         a.ws_o = reinterpret_cast<float *>(ws);
         a.ws_lse = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + plan.ws_lse_offset);
-        a.direct = 0;
     } else {
         a.ws_o = nullptr;
         a.ws_lse = nullptr;
-        a.direct = 1;
     }
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
     fd::LaunchShape shape{dim3(plan.grid_x, plan.grid_y, plan.grid_z), dim3(plan.threads)};
 
-    if (opt && opt->split_begin_event) {
-        if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_begin_event), stream) != hipSuccess)
-            return fail(FD_ERR_LAUNCH, "hipEventRecord(split_begin_event) failed");
-    }
+    hipEvent_t ev0 = opt ? reinterpret_cast<hipEvent_t>(opt->split_begin_event) : nullptr;
+    hipEvent_t ev1 = opt ? reinterpret_cast<hipEvent_t>(opt->split_end_event) : nullptr;
     a.heads_per_wg = plan.heads_per_group;
     // 16-token blocks stay inside one page when pages hold at least 16 tokens.
     const int mode = !paged ? fd::kContig : ((1 << a.page_shift) >= 16 ? fd::kPagedBlock : fd::kPagedRow);
     hipError_t e = plan.kernel == FD_KERNEL_MFMA
-                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, shape, a, stream)
-                       : fd::launch_split_valu(dtype, plan.heads_per_group, mode, shape, a, stream);
+                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, shape, a, stream, ev0, ev1)
+                       : fd::launch_split_valu(dtype, plan.heads_per_group, mode, shape, a, stream, ev0, ev1);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
-    if (opt && opt->split_end_event) {
-        if (hipEventRecord(reinterpret_cast<hipEvent_t>(opt->split_end_event), stream) != hipSuccess)
-            return fail(FD_ERR_LAUNCH, "hipEventRecord(split_end_event) failed");
-    }
     if (plan.merge) {
         m.ws_o = a.ws_o;
         m.ws_lse = a.ws_lse;

@@ -214,4 +214,122 @@ __device__ __forceinline__ uint4 load_stream16_at(const T *base, size_t byte_off
 // "FlashAttention：分块 + online softmax"). An empty state has m = -inf, l = 0.
 __device__ __forceinline__ float finite_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
 
+// ---------------------------------------------------------------- LSE merge
+// One wave merges the n partials of one (sequence, head): split s holds a
+// normalised output O_s (ws row s) and the natural-log lse_s of its scores.
+// With M = max lse_s and w_s = exp(lse_s - M): o = sum w_s O_s / sum w_s
+// ("[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节";
+// equal to the (m, l) merge of "FlashAttention 与推理算子", section "decode 阶段的
+// 并行：Flash-Decoding 与 split-K", since lse_s = m_s + ln l_s). Each lane owns
+// two adjacent output elements. Splits go in batches of kMergeBatch: the
+// batch's partial rows and lse values are all loaded before any of them is
+// used, so a batch costs one round trip to memory; lane i holds split
+// s0 + i's weight and readlane broadcasts it. n == 0 gives 0.
+constexpr int kMergeBatch = 32;
+
+__device__ __forceinline__ float2 merge_partials(const float *ws_o_row, const float *lse_row, int n, int lane) {
+    const float2 *src = reinterpret_cast<const float2 *>(ws_o_row) + lane;
+    // max lse over all splits
+    float mx = -INFINITY;
+    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_row[s]);
+    float o0 = 0.f, o1 = 0.f, wpart = 0.f;
+    float mu = 0.f;
+    for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+        const int cnt = min(kMergeBatch, n - s0);
+        // Rows past the batch re-read its last row (a valid address) and get
+        // weight 0, so every load is unconditional.
+        float2 x[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) x[u] = src[(size_t)(s0 + min(u, cnt - 1)) * (kHeadDim / 2)];
+        const float l = lane < cnt ? lse_row[s0 + lane] : -INFINITY;
+        if (s0 == 0) mu = finite_or_zero(wave_max(mx));
+        const float w = lane < cnt ? exp2_fast((l - mu) * kLog2e) : 0.f;
+        wpart += w;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+            o0 = __builtin_fmaf(wu, x[u].x, o0);
+            o1 = __builtin_fmaf(wu, x[u].y, o1);
+        }
+    }
+    const float wsum = wave_sum(wpart);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    return make_float2(o0 * inv, o1 * inv);
+}
+
+template <typename T>
+struct Pair;
+template <>
+struct Pair<float> {
+    typedef float2 type;
+    __device__ static type make(float a, float b) { return make_float2(a, b); }
+};
+template <>
+struct Pair<__bf16> {
+    typedef __bf16 type __attribute__((ext_vector_type(2)));
+    __device__ static type make(float a, float b) { return type{(__bf16)a, (__bf16)b}; }
+};
+template <>
+struct Pair<_Float16> {
+    typedef _Float16 type __attribute__((ext_vector_type(2)));
+    __device__ static type make(float a, float b) { return type{(_Float16)a, (_Float16)b}; }
+};
+
+// Output row (b, h) elements 2*lane, 2*lane + 1, rounded to T (nearest even).
+template <typename T>
+__device__ __forceinline__ void store_out_pair(void *out, size_t bh, int lane, float2 v) {
+    typedef typename Pair<T>::type P2;
+    reinterpret_cast<P2 *>(reinterpret_cast<T *>(out) + bh * kHeadDim)[lane] = Pair<T>::make(v.x, v.y);
+}
+
+// ---------------------------------------------------------------- split prologue
+// Length of sequence b and, for a paged cache, the split's slice of its block
+// table staged in LDS (entries clamped into [0, num_pages)). The table loads
+// are issued together with the length load, before the length is known: the
+// slice read is bounded by the table row, not by L_b, so both cost one round
+// trip. Every thread of the workgroup must call this (it holds a barrier).
+// Returns L_b clamped to [0, max_len]; *page_first is the table index of
+// s_pages[0].
+template <bool PAGED>
+__device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_begin, int *s_pages, int *page_first) {
+    if constexpr (!PAGED) {
+        *page_first = 0;
+        return a.max_len;
+    } else {
+        const int L_raw = a.seq_lens[b];
+        const int first = t_begin >> a.page_shift;
+        const int last = min((t_begin + a.chunk - 1) >> a.page_shift, a.max_blocks - 1);
+        const int32_t *row = a.block_table + (size_t)b * a.max_blocks + first;
+        for (int i = threadIdx.x; i <= last - first; i += blockDim.x) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
+        __syncthreads();
+        *page_first = first;
+        return max(0, min(L_raw, a.max_len));
+    }
+}
+
+// ---------------------------------------------------------------- split epilogue
+// Stores one workgroup's result for query heads h0 .. h0+nh-1 of sequence b,
+// split `split` of n_b. value(hh, d, lse) returns the split's normalised
+// output element and sets its natural-log lse. When n_b == 1 the split is the
+// whole sequence and o is written directly; otherwise the partial goes to the
+// workspace for the merge kernel.
+template <typename T, typename ValueFn>
+__device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int split, int n_b, ValueFn value) {
+    const bool direct = n_b == 1;
+    for (int i = threadIdx.x; i < nh * kHeadDim; i += blockDim.x) {
+        const int hh = i / kHeadDim;
+        const int d = i - hh * kHeadDim;
+        float lse;
+        const float o = value(hh, d, lse);
+        const size_t bh = (size_t)b * a.H + h0 + hh;
+        if (direct) {
+            reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = Elem<T>::store_cast(o);
+        } else {
+            const size_t row = bh * a.num_splits + split;
+            a.ws_o[row * kHeadDim + d] = o;
+            if (d == 0) a.ws_lse[row] = lse;
+        }
+    }
+}
+
 }  // namespace fd

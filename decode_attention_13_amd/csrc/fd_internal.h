@@ -2,6 +2,7 @@
 // launchers. Not part of the public interface.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -28,7 +29,7 @@ struct SplitArgs {
     const int32_t *seq_lens;     // [B] (paged)
     float *ws_o;            // [B, H, num_splits, D]
     float *ws_lse;          // [B, H, num_splits]
-    void *out;              // [B, H, D] (direct mode)
+    void *out;              // [B, H, D]
     int H, Hkv, G;          // G = H / Hkv
     int heads_per_wg;       // query heads of one KV head computed by one workgroup
     int max_len;            // contiguous: S; paged: clamp bound for seq_lens
@@ -37,7 +38,6 @@ struct SplitArgs {
     int page_shift;         // log2(page_size)
     int max_blocks;
     int num_pages;
-    int direct;             // 1: write o (single split), 0: write partials
     float scale_log2;       // scale * log2(e)
 };
 
@@ -59,10 +59,19 @@ struct LaunchShape {
 
 // Each returns hipSuccess or the launch error. `gt` = heads per workgroup,
 // `mode` = AddrMode of fd_device.h (contiguous, paged by 16-token block, paged by row).
+// `start`/`stop` (may be NULL) are timestamped by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernel), so they time the kernel alone.
 hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
-                             hipStream_t stream);
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
-                             hipStream_t stream);
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+// Launch through hipExtLaunchKernel when events are given, else hipLaunchKernel.
+inline hipError_t launch_timed(const void *fn, const LaunchShape &s, void **args, hipStream_t st, hipEvent_t start,
+                               hipEvent_t stop) {
+    if (start || stop) return hipExtLaunchKernel(fn, s.grid, s.block, args, 0, st, start, stop, 0);
+    return hipLaunchKernel(fn, s.grid, s.block, args, 0, st);
+}
 hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, hipStream_t stream);
 
 }  // namespace fd

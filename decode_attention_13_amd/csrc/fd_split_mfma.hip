@@ -101,11 +101,11 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     __shared__ float s_m[kWaves][kMaxHeads];
     __shared__ float s_l[kWaves][kMaxHeads];
 
-    int L = a.max_len;
-    if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
     const int t_begin = split * a.chunk;
-    if (t_begin >= L) {
-        if (a.direct && split == 0) {
+    int page_first = 0;
+    const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
+    if (t_begin >= L) {  // uniform over the workgroup
+        if (split == 0) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
@@ -113,14 +113,6 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     }
     const int t_end = min(t_begin + a.chunk, L);
 
-    int page_first = 0;
-    if (PAGED) {
-        page_first = t_begin >> a.page_shift;
-        const int n_pages = ((t_end - 1) >> a.page_shift) - page_first + 1;
-        const int32_t *row = a.block_table + (size_t)b * a.max_blocks + page_first;
-        for (int i = threadIdx.x; i < n_pages; i += kThreads) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
-        __syncthreads();
-    }
     const T *kbase = reinterpret_cast<const T *>(a.k);
     const T *vbase = reinterpret_cast<const T *>(a.v);
     KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(T),
@@ -299,9 +291,8 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) {
-        const int hh = i / kHeadDim;
-        const int d = i - hh * kHeadDim;
+    const int n_b = (L + a.chunk - 1) / a.chunk;
+    finish_split<T>(a, b, h0, nh, split, n_b, [&](int hh, int d, float &lse) {
         float Mx = s_m[0][hh];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][hh]);
@@ -313,31 +304,25 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
             l = __builtin_fmaf(wgt, s_l[w][hh], l);
             o = __builtin_fmaf(wgt, s_acc[(w * kMaxHeads + hh) * kHeadDim + d], o);
         }
-        const float out = o / l;
-        const size_t bh = (size_t)b * a.H + h0 + hh;
-        if (a.direct) {
-            reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = E::store_cast(out);
-        } else {
-            const size_t row = bh * a.num_splits + split;
-            a.ws_o[row * kHeadDim + d] = out;
-            if (d == 0) a.ws_lse[row] = (Mx + log2_fast(l)) * kLn2;
-        }
-    }
+        lse = (Mx + log2_fast(l)) * kLn2;
+        return o / l;
+    });
 }
 
 template <typename T, int MODE>
-hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&split_mfma_kernel<T, MODE>), s.grid, s.block, args, 0, st);
+    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, MODE>), s, args, st, e0, e1);
 }
 
 template <typename T>
-hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_one<T, kContig>(s, a, st);
-        case kPagedBlock: return launch_one<T, kPagedBlock>(s, a, st);
-        case kPagedRow: return launch_one<T, kPagedRow>(s, a, st);
+        case kContig: return launch_one<T, kContig>(s, a, st, e0, e1);
+        case kPagedBlock: return launch_one<T, kPagedBlock>(s, a, st, e0, e1);
+        case kPagedRow: return launch_one<T, kPagedRow>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -345,11 +330,11 @@ hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipSt
 }  // namespace
 
 hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
-                             hipStream_t st) {
+                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if (gt < 1 || gt > kMaxHeads) return hipErrorInvalidValue;
     switch (dtype) {
-        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, s, a, st);
-        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, s, a, st);
+        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

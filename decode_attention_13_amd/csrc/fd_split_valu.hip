@@ -51,26 +51,17 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     __shared__ float s_l[kWaves][GT];
     __shared__ float s_acc[kWaves][GT][kHeadDim];
 
-    int L = a.max_len;
-    if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
     const int t_begin = split * a.chunk;
+    int page_first = 0;
+    const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
     if (t_begin >= L) {  // uniform over the workgroup
-        if (a.direct && split == 0) {  // empty sequence: o = 0
+        if (split == 0) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = threadIdx.x; i < GT * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
         return;
     }
     const int t_end = min(t_begin + a.chunk, L);
-
-    int page_first = 0;
-    if (PAGED) {
-        page_first = t_begin >> a.page_shift;
-        const int n_pages = ((t_end - 1) >> a.page_shift) - page_first + 1;
-        const int32_t *row = a.block_table + (size_t)b * a.max_blocks + page_first;
-        for (int i = threadIdx.x; i < n_pages; i += kThreads) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
-        __syncthreads();
-    }
 
     const T *kbase = reinterpret_cast<const T *>(a.k);
     const T *vbase = reinterpret_cast<const T *>(a.v);
@@ -226,10 +217,9 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     }
     __syncthreads();
 
-    // Merge the waves and store: one thread per (head, element).
-    for (int i = threadIdx.x; i < GT * kHeadDim; i += kThreads) {
-        const int gi = i / kHeadDim;
-        const int d = i - gi * kHeadDim;
+    // Merge the waves, then store the split (or the merged output).
+    const int n_b = (L + a.chunk - 1) / a.chunk;
+    finish_split<T>(a, b, h0, GT, split, n_b, [&](int gi, int d, float &lse) {
         float M = s_m[0][gi];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gi]);
@@ -241,43 +231,36 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             lsum = __builtin_fmaf(wgt, s_l[w][gi], lsum);
             o = __builtin_fmaf(wgt, s_acc[w][gi][d], o);
         }
-        const float out = o / lsum;
-        const size_t bh = (size_t)b * a.H + h0 + gi;
-        if (a.direct) {
-            reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = E::store_cast(out);
-        } else {
-            const size_t row = bh * a.num_splits + split;
-            a.ws_o[row * kHeadDim + d] = out;
-            if (d == 0) a.ws_lse[row] = (M + log2_fast(lsum)) * kLn2;
-        }
-    }
+        lse = (M + log2_fast(lsum)) * kLn2;
+        return o / lsum;
+    });
 }
 
 template <typename T, int GT, int MODE>
-hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, MODE>), s.grid, s.block, args, 0,
-                           st);
+    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, MODE>), s, args, st, e0, e1);
 }
 
 template <typename T, int MODE>
-hipError_t launch_gt(int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+hipError_t launch_gt(int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (gt) {
-        case 1: return launch_one<T, 1, MODE>(s, a, st);
-        case 2: return launch_one<T, 2, MODE>(s, a, st);
-        case 4: return launch_one<T, 4, MODE>(s, a, st);
-        case 8: return launch_one<T, 8, MODE>(s, a, st);
+        case 1: return launch_one<T, 1, MODE>(s, a, st, e0, e1);
+        case 2: return launch_one<T, 2, MODE>(s, a, st, e0, e1);
+        case 4: return launch_one<T, 4, MODE>(s, a, st, e0, e1);
+        case 8: return launch_one<T, 8, MODE>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st) {
+hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_gt<T, kContig>(gt, s, a, st);
-        case kPagedBlock: return launch_gt<T, kPagedBlock>(gt, s, a, st);
-        case kPagedRow: return launch_gt<T, kPagedRow>(gt, s, a, st);
+        case kContig: return launch_gt<T, kContig>(gt, s, a, st, e0, e1);
+        case kPagedBlock: return launch_gt<T, kPagedBlock>(gt, s, a, st, e0, e1);
+        case kPagedRow: return launch_gt<T, kPagedRow>(gt, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -285,11 +268,11 @@ hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &
 }  // namespace
 
 hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
-                             hipStream_t st) {
+                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (dtype) {
-        case FD_DTYPE_F32: return launch_mode<float>(mode, gt, s, a, st);
-        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, gt, s, a, st);
-        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, gt, s, a, st);
+        case FD_DTYPE_F32: return launch_mode<float>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, gt, s, a, st, e0, e1);
     }
     return hipErrorInvalidValue;
 }

@@ -63,8 +63,9 @@ typedef enum fd_status {
 enum {
     FD_KERNEL_AUTO = 0, /* planner's choice */
     FD_KERNEL_VALU = 1, /* vector-ALU split kernel (any head group, every dtype) */
-    FD_KERNEL_MFMA = 2  /* matrix-core split kernel (f16/bf16, H/Hkv in {4, 8, 16}) */
+    FD_KERNEL_MFMA = 2  /* matrix-core split kernel (f16/bf16, H/Hkv <= 16 or a multiple of 16) */
 };
+
 
 /* Optional knobs; pass NULL for all defaults. Zero means "automatic". */
 typedef struct fd_options {
@@ -72,8 +73,9 @@ typedef struct fd_options {
     int force_chunk;      /* > 0: tokens per split, a multiple of FD_CHUNK_QUANTUM (wins over force_num_splits) */
     int force_kernel;     /* FD_KERNEL_* */
     int reserved;         /* must be 0 */
-    void *split_begin_event; /* hipEvent_t recorded on `stream` right before the split kernel, or NULL */
-    void *split_end_event;   /* hipEvent_t recorded on `stream` right after the split kernel, or NULL */
+    void *split_begin_event; /* hipEvent_t stamped when the split kernel starts executing, or NULL */
+    void *split_end_event;   /* hipEvent_t stamped when the split kernel finishes, or NULL
+                                (both set by the dispatch itself: hipExtLaunchKernel) */
 } fd_options;
 
 /* What a call with the same arguments would launch. */
@@ -84,21 +86,23 @@ typedef struct fd_plan {
     int num_splits;      /* splits of the longest sequence = grid y */
     int grid_x, grid_y, grid_z; /* split kernel grid: (KV-head slices, splits, sequences) */
     int threads;         /* split kernel workgroup size */
-    int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: direct output */
+    int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: o written directly */
     int reserved;
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
-    size_t ws_lse_offset;   /* byte offset of the lse array inside the workspace */
+    size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
 } fd_plan;
 
 /*
- * Workspace layout when merge == 1 (fp32, row-major, from byte 0):
+ * Workspace layout when merge == 1 (fp32, row-major, from byte 0; no
+ * initialisation needed):
  *   ws_o  [B, H, num_splits, D]  normalised output of each split
  *   ws_lse[B, H, num_splits]     natural-log log-sum-exp of each split's scores,
  *                                at byte offset ws_lse_offset.
- * Split s of sequence b covers tokens [s*chunk, min((s+1)*chunk, L_b)); only
- * splits s < ceil(L_b / chunk) are written. The split kernel stores partials the
- * way "[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节"
- * describes (normalised output plus log-sum-exp per split).
+ * Split s of sequence b covers tokens [s*chunk, min((s+1)*chunk, L_b)). Only
+ * the splits s < ceil(L_b / chunk) of sequences with more than one split are
+ * written; a sequence that fits one split is written to o directly. The split
+ * kernel stores partials as "[CUDA 优化实战] 纯手搓 flash decoding sm120",
+ * section "2. kernel 实现细节" describes: normalised output plus log-sum-exp.
  */
 
 /* Compute units of the current HIP device (cached per device); -1 on error. */
