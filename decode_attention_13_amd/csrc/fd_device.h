@@ -227,24 +227,22 @@ __device__ __forceinline__ float finite_or_zero(float m) { return m == -INFINITY
 // s0 + i's weight and readlane broadcasts it. n == 0 gives 0.
 constexpr int kMergeBatch = 32;
 
-__device__ __forceinline__ float2 merge_partials(const float *ws_o_row, const float *lse_row, int n, int lane) {
+// Partial sums of one wave over splits [s_lo, s_hi) against a given max mu:
+// returns (sum w_s O_s[2 lane], sum w_s O_s[2 lane + 1]) and adds this lane's
+// share of sum w_s to *wpart.
+__device__ __forceinline__ float2 merge_range(const float *ws_o_row, const float *lse_row, int s_lo, int s_hi,
+                                              float mu, int lane, float *wpart) {
     const float2 *src = reinterpret_cast<const float2 *>(ws_o_row) + lane;
-    // max lse over all splits
-    float mx = -INFINITY;
-    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_row[s]);
-    float o0 = 0.f, o1 = 0.f, wpart = 0.f;
-    float mu = 0.f;
-    for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
-        const int cnt = min(kMergeBatch, n - s0);
+    float o0 = 0.f, o1 = 0.f;
+    for (int s0 = s_lo; s0 < s_hi; s0 += kMergeBatch) {
+        const int cnt = min(kMergeBatch, s_hi - s0);
         // Rows past the batch re-read its last row (a valid address) and get
         // weight 0, so every load is unconditional.
         float2 x[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) x[u] = src[(size_t)(s0 + min(u, cnt - 1)) * (kHeadDim / 2)];
-        const float l = lane < cnt ? lse_row[s0 + lane] : -INFINITY;
-        if (s0 == 0) mu = finite_or_zero(wave_max(mx));
-        const float w = lane < cnt ? exp2_fast((l - mu) * kLog2e) : 0.f;
-        wpart += w;
+        const float w = lane < cnt ? exp2_fast((lse_row[s0 + lane] - mu) * kLog2e) : 0.f;
+        *wpart += w;
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
@@ -252,9 +250,19 @@ __device__ __forceinline__ float2 merge_partials(const float *ws_o_row, const fl
             o1 = __builtin_fmaf(wu, x[u].y, o1);
         }
     }
+    return make_float2(o0, o1);
+}
+
+// Whole merge of one (sequence, head) by a single wave.
+__device__ __forceinline__ float2 merge_partials(const float *ws_o_row, const float *lse_row, int n, int lane) {
+    float mx = -INFINITY;
+    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_row[s]);
+    const float mu = finite_or_zero(wave_max(mx));
+    float wpart = 0.f;
+    const float2 o = merge_range(ws_o_row, lse_row, 0, n, mu, lane, &wpart);
     const float wsum = wave_sum(wpart);
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    return make_float2(o0 * inv, o1 * inv);
+    return make_float2(o.x * inv, o.y * inv);
 }
 
 template <typename T>

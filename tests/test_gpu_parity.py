@@ -330,6 +330,17 @@ def test_paged_split_invariance(device):
         assert_close(o, ref, "f16", f"paged chunk {plan['chunk']}")
 
 
+@pytest.mark.parametrize("H,Hkv,S,chunk", [(1, 1, 131072, 128), (2, 1, 65600, 64), (4, 2, 40000, 1024)])
+def test_many_splits(H, Hkv, S, chunk, device):
+    """Up to 2048 splits per head: the merge kernel splits the work across its waves."""
+    d = inputs.single_inputs(H, Hkv, S, 128, "bf16", 300 + S, peak_frac=0.01)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    for kernel in ("valu", "mfma"):
+        announce(f"many splits H={H} S={S} chunk={chunk} {kernel}")
+        o = run_single(d, device, opt=fd.options(force_chunk=chunk, kernel=kernel))
+        assert_close(o, ref, "bf16", f"H={H} S={S} chunk={chunk} {kernel}")
+
+
 def test_workspace_reuse_across_plans(device):
     """One uninitialised workspace (filled with NaN) serves calls of different plans in
     any order: nothing is read from it that the same call did not write."""
