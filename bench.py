@@ -10,7 +10,7 @@ bytes / step time), the dominant kernel's roofline (its own launch durations
 timed with HIP events on the stream it runs on) and the float64 CPU oracle's
 throughput on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--sweep] [--no-cpu-baseline]
   python bench.py --copy-probe BYTES   # a plain device copy, to scale rocprof byte counters
 """
 from __future__ import annotations
@@ -30,7 +30,7 @@ METRIC = "decode µs/step + achieved HBM GB/s (fraction of peak), KV 4k→128k"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 COLD_BYTES = 512 << 20      # bytes touched between reuses of one KV copy
 DEFAULT_WORKLOAD = "decode_bf16_h32_s4096"
-SPLIT_KERNEL = "split_valu_kernel"
+SPLIT_KERNELS = {1: "split_valu_kernel", 2: "split_mfma_kernel"}  # by fd_plan.kernel
 SWEEP = (4096, 8192, 16384, 32768, 65536, 131072, 131073)
 
 
@@ -49,9 +49,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str) -> dict | None:
+def load_traffic(kernel: str, workload: str) -> dict | None:
     """HBM bytes per split-kernel launch from the committed rocprofv3 --pmc summary."""
-    path = os.path.join(ROOT, "profiles", f"{SPLIT_KERNEL}_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
@@ -64,7 +64,7 @@ def load_traffic(workload: str) -> dict | None:
 class Case:
     """A workload placed in device memory with rotated KV copies and its C-ABI arguments."""
 
-    def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None):
+    def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None, kv: str = "native"):
         import torch
 
         import decode_attention_13_amd as fd
@@ -77,22 +77,29 @@ class Case:
         if data is None:
             log(f"generating {w.name}")
             data = w.make()
+        self.fp8 = kv == "fp8"
+        if self.fp8:
+            from decode_attention_13_amd.inputs import with_fp8_kv
+            data = with_fp8_kv(data)
         d = data
         self.d = d
         self.opt = fd.options(force_chunk=chunk, kernel=kernel) if (chunk or kernel != "auto") else None
-        esize = torch.tensor([], dtype=inputs_dtype(w.dtype)).element_size()
-        self.dtype_code = binding.FD_DTYPE[inputs_dtype(w.dtype)]
+        qdt = inputs_dtype(w.dtype)
+        esize = 1 if self.fp8 else torch.tensor([], dtype=qdt).element_size()
+        self.dtype_code = binding.FD_DTYPE_KV_E4M3[qdt] if self.fp8 else binding.FD_DTYPE[qdt]
+        self.dtype_name = f"{w.dtype}_kv_e4m3" if self.fp8 else w.dtype
         if w.kind == "single":
             self.kv_bytes = 2 * w.S * w.Hkv * 128 * esize
             self.units = w.S * w.Hkv
-            self.plan = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 0, self.opt)
+            self.plan = fd.decode_plan(w.H, w.Hkv, w.S, self.dtype_code, 0, self.opt)
             self.q = d["q"].to(dev)
             srcs = (d["k"], d["v"])
         else:
             self.total = d["total_kv"]
             self.kv_bytes = 2 * self.total * w.Hkv * 128 * esize
             self.units = self.total * w.Hkv
-            self.plan = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, d["max_seq_len"], self.total, 0, self.opt)
+            self.plan = fd.paged_plan(w.B, w.H, w.Hkv, self.dtype_code, w.page_size, d["max_seq_len"], self.total, 0,
+                                      self.opt)
             self.q = d["q"].to(dev)
             self.table = d["block_table"].to(dev)
             self.lens = d["seq_lens"].to(dev)
@@ -111,10 +118,22 @@ class Case:
         o = opt if opt is not None else self.opt
         optp = ctypes.byref(o) if o is not None else None
         w = self.w
-        if w.kind == "single":
+        if w.kind == "single" and self.fp8:
+            rc = self.lib.fd_decode_fp8kv(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), w.H, w.Hkv,
+                                          w.S, 128, self.dtype_code, self.d["scale"], self.d["k_scale"],
+                                          self.d["v_scale"], self.ws.data_ptr(), self.ws.numel(), optp,
+                                          self.stream.cuda_stream)
+        elif w.kind == "single":
             rc = self.lib.fd_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), w.H, w.Hkv, w.S,
                                     128, self.dtype_code, self.d["scale"], self.ws.data_ptr(),
                                     self.ws.numel(), optp, self.stream.cuda_stream)
+        elif self.fp8:
+            rc = self.lib.fd_paged_decode_fp8kv(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.table.data_ptr(),
+                                                self.lens.data_ptr(), w.page_size, self.o.data_ptr(), self.d["scale"],
+                                                self.d["k_scale"], self.d["v_scale"], w.B, w.H, w.Hkv, 128,
+                                                self.d["num_pages"], self.d["max_blocks"], self.d["max_seq_len"],
+                                                self.total, self.dtype_code, self.ws.data_ptr(), self.ws.numel(),
+                                                optp, self.stream.cuda_stream)
         else:
             rc = self.lib.fd_paged_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.table.data_ptr(),
                                           self.lens.data_ptr(), w.page_size, self.o.data_ptr(), self.d["scale"], w.B,
@@ -164,8 +183,9 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
             "split_median_s": split_ms[len(split_ms) // 2] / 1e3}
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The float64 oracle as it stands, timed on this host over a bounded sample."""
+def cpu_baseline(w, budget_s: float = 12.0, fp8: bool = False) -> dict:
+    """The float64 oracle as it stands, timed on this host over a bounded sample
+    (the E4M3 form of the oracle when the cache is FP8)."""
     import numpy as np
 
     import oracle
@@ -175,13 +195,20 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     except Exception:  # pragma: no cover
         threads = 1
     d = w.make()
+    if fp8:
+        from decode_attention_13_amd.inputs import with_fp8_kv
+        d = with_fp8_kv(d)
     if w.kind == "single":
         heads = list(range(w.H))
         n_done = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             h = heads[n_done % len(heads)]
-            oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=[h])
+            if fp8:
+                oracle.decode_attention_e4m3(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["scale"],
+                                             heads=[h])
+            else:
+                oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=[h])
             n_done += 1
         el = time.perf_counter() - t0
         sample = f"{n_done} single-head decodes of {w.name} (S={w.S}), {el:.1f} s"
@@ -193,16 +220,27 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             b = int(rng.integers(w.B))
-            oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
-                                          d["page_size"], d["scale"], pairs=[(b, h) for h in range(w.H)])
+            pairs = [(b, h) for h in range(w.H)]
+            if fp8:
+                oracle.paged_decode_attention_e4m3(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                                   d["seq_lens"], d["page_size"], d["k_scale"], d["v_scale"],
+                                                   d["scale"], pairs=pairs)
+            else:
+                oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                              d["page_size"], d["scale"], pairs=pairs)
             n_done += 1
             tokens_done += int(lens[b])
         el = time.perf_counter() - t0
         sample = f"{n_done} whole sequences (all {w.H} heads) of {w.name}, {el:.1f} s"
         step_s = el / tokens_done * float(lens.sum())
-    kv_bytes = w.kv_bytes()
+    kv_bytes = 2 * _kv_elems(w, d) if fp8 else w.kv_bytes()  # E4M3: one byte per element
     return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": sample, "us_per_step": round(step_s * 1e6, 1)}
+
+
+def _kv_elems(w, d) -> int:
+    """K (or V) elements of a workload."""
+    return (w.S if w.kind == "single" else int(d["total_kv"])) * w.Hkv * 128
 
 
 def copy_probe(nbytes: int, steps: int) -> None:
@@ -224,6 +262,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--chunk", type=int, default=0, help="force tokens per split (multiple of 64)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"], help="force the split kernel")
+    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
+                    help="cache storage: the workload's dtype, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--sweep", action="store_true", help="also time the pages' KV-length sweep (4k..128k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
@@ -244,12 +284,14 @@ def main() -> int:
 
     from decode_attention_13_amd.inputs import WORKLOADS, sweep_workload
     w = WORKLOADS[args.workload]
-    case = Case(w, args.chunk, args.kernel)
+    case = Case(w, args.chunk, args.kernel, kv=args.kv)
+    split_kernel = SPLIT_KERNELS[case.plan["kernel"]]
+    wl_name = w.name + ("_kv_e4m3" if case.fp8 else "")
     t = time_steps(case, args.steps, args.warmup)
     step_s = t["wall_s"]
     split_s = t["split_mean_s"]
     achieved = case.kv_bytes / split_s / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(split_kernel, wl_name)
     line = {
         "metric": METRIC,
         "value": round(case.kv_bytes / step_s / 1e9, 2),
@@ -263,24 +305,25 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": case.dtype_name,
         "data": "synthetic",
-        "config": {"workload": w.name, "kv_bytes": case.kv_bytes, "plan": case.plan, "kv_copies": case.copies,
+        "config": {"workload": wl_name, "kv_bytes": case.kv_bytes, "plan": case.plan, "kv_copies": case.copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
-                     "kernel": SPLIT_KERNEL, "kernel_us_mean": round(split_s * 1e6, 3),
+                     "kernel": split_kernel, "kernel_us_mean": round(split_s * 1e6, 3),
                      "kernel_us_median": round(t["split_median_s"] * 1e6, 3),
                      "bytes_per_launch": case.kv_bytes,
                      "bytes_per_unit": case.kv_bytes // case.units, "units_per_launch": case.units},
     }
+    case_fp8 = case.fp8
     del case
     torch.cuda.empty_cache()
     if args.sweep:
         sweep = []
         for S in SWEEP:
-            c = Case(sweep_workload(S))
+            c = Case(sweep_workload(S), kv=args.kv)
             ts = time_steps(c, max(20, args.steps // 4), 5)
             sweep.append({"S": S, "us_per_step": round(ts["wall_s"] * 1e6, 2),
                           "GBps": round(c.kv_bytes / ts["wall_s"] / 1e9, 1),
@@ -291,7 +334,7 @@ def main() -> int:
         line["sweep"] = sweep
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, fp8=case_fp8)
     print(json.dumps(line), flush=True)
     return 0
 

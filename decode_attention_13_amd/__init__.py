@@ -10,7 +10,9 @@ from .binding import (  # noqa: F401
     decode_plan,
     device_num_cus,
     fd_decode,
+    fd_decode_fp8kv,
     fd_paged_decode,
+    fd_paged_decode_fp8kv,
     lib,
     new_workspace,
     options,

@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libfd.so")
 
 FD_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 DTYPE_NAMES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# FP8 E4M3 caches: code by query dtype, and by name
+FD_DTYPE_KV_E4M3 = {torch.float16: 3, torch.bfloat16: 4}
+FP8_CODES = {"f16_kv_e4m3": 3, "bf16_kv_e4m3": 4}
+FP8_CACHE_DTYPES = (torch.float8_e4m3fn, torch.uint8)  # uint8 = raw E4M3 codes
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 HEAD_DIM = 128
 CHUNK_QUANTUM = 64
@@ -67,6 +71,16 @@ SIGNATURES = {
                                        ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(FdOptions),
                                        ctypes.c_void_p]),
+    "fd_decode_fp8kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.POINTER(FdOptions), ctypes.c_void_p]),
+    "fd_paged_decode_fp8kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_float,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.POINTER(FdOptions), ctypes.c_void_p]),
     "fd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fd_last_error": (ctypes.c_char_p, []),
 }
@@ -110,11 +124,22 @@ def _opt_ptr(opt):
 
 
 def _dtype_code(dt) -> int:
+    """fd_dtype code of a torch dtype, a name ("bf16", "f16_kv_e4m3", ...) or a code."""
+    if isinstance(dt, int):
+        return dt
     if isinstance(dt, str):
+        if dt in FP8_CODES:
+            return FP8_CODES[dt]
         dt = DTYPE_NAMES[dt]
     if dt not in FD_DTYPE:
         raise TypeError(f"unsupported dtype {dt}")
     return FD_DTYPE[dt]
+
+
+def _fp8_code(q_dtype) -> int:
+    if q_dtype not in FD_DTYPE_KV_E4M3:
+        raise TypeError(f"an FP8 cache needs f16 or bf16 queries, not {q_dtype}")
+    return FD_DTYPE_KV_E4M3[q_dtype]
 
 
 def device_num_cus() -> int:
@@ -163,29 +188,80 @@ def _workspace(ws, need: int, device) -> tuple[int, int, torch.Tensor | None]:
     return ws.data_ptr(), ws.numel() * ws.element_size(), ws
 
 
-def fd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
-              scale: float | None = None, ws: torch.Tensor | None = None, opt: FdOptions | None = None,
-              stream=None) -> torch.Tensor:
-    """Single decode over a contiguous cache: q [H, D], k/v [S, Hkv, D] -> o [H, D]."""
+def _single_args(q, k, v, o, kv_dtype):
     H, D = q.shape
     S, Hkv, Dk = k.shape
     if v.shape != k.shape or Dk != D:
         raise ValueError("k and v must both be [S, Hkv, D] with q's D")
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n, q.dtype)
+    _require(q, "q", q.dtype)
+    for t, n in ((k, "k"), (v, "v")):
+        _require(t, n, kv_dtype)
     if o is None:
         o = torch.empty_like(q)
     _require(o, "o", q.dtype)
     if o.shape != q.shape:
         raise ValueError("o must have q's shape")
+    return H, Hkv, S, D, o
+
+
+def fd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+              scale: float | None = None, ws: torch.Tensor | None = None, opt: FdOptions | None = None,
+              stream=None) -> torch.Tensor:
+    """Single decode over a contiguous cache: q [H, D], k/v [S, Hkv, D] -> o [H, D]."""
+    H, Hkv, S, D, o = _single_args(q, k, v, o, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dt = _dtype_code(q.dtype)
-    plan = decode_plan(H, Hkv, S, q.dtype, 0, opt)
+    plan = decode_plan(H, Hkv, S, dt, 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
     _check(lib().fd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), H, Hkv, S, D, dt, float(scale),
                            wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
     return o
+
+
+def _fp8_cache_dtype(t: torch.Tensor, name: str) -> torch.dtype:
+    if t.dtype not in FP8_CACHE_DTYPES:
+        raise TypeError(f"{name} must hold E4M3 codes (float8_e4m3fn or uint8), not {t.dtype}")
+    return t.dtype
+
+
+def fd_decode_fp8kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_scale: float, v_scale: float,
+                    o: torch.Tensor | None = None, scale: float | None = None, ws: torch.Tensor | None = None,
+                    opt: FdOptions | None = None, stream=None) -> torch.Tensor:
+    """Single decode over an FP8 E4M3 cache: K = k_scale * E4M3(k), V = v_scale * E4M3(v);
+    q [H, D] f16/bf16, k/v [S, Hkv, D] codes -> o [H, D] in q's dtype."""
+    H, Hkv, S, D, o = _single_args(q, k, v, o, _fp8_cache_dtype(k, "k"))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = _fp8_code(q.dtype)
+    plan = decode_plan(H, Hkv, S, dt, 0, opt)
+    wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    _check(lib().fd_decode_fp8kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), H, Hkv, S, D, dt,
+                                 float(scale), float(k_scale), float(v_scale), wp or None, wb, _opt_ptr(opt),
+                                 _stream_handle(stream)))
+    return o
+
+
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, kv_dtype):
+    B, H, D = q.shape
+    num_pages, ps, Hkv, Dk = k_cache.shape
+    if page_size is None:
+        page_size = ps
+    if v_cache.shape != k_cache.shape or Dk != D or ps != page_size:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, D]")
+    _require(q, "q", q.dtype)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n, kv_dtype)
+    _require(block_table, "block_table", torch.int32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", q.dtype)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    return B, H, Hkv, D, num_pages, page_size, block_table.shape[1], int(max_seq_len), o
 
 
 def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -198,34 +274,40 @@ def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     ``max_seq_len`` must bound every entry of ``seq_lens``; if omitted it is read
     from the device (a synchronising copy).
     """
-    B, H, D = q.shape
-    num_pages, ps, Hkv, Dk = k_cache.shape
-    if page_size is None:
-        page_size = ps
-    if v_cache.shape != k_cache.shape or Dk != D or ps != page_size:
-        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, D]")
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _require(t, n, q.dtype)
-    _require(block_table, "block_table", torch.int32)
-    _require(seq_lens, "seq_lens", torch.int32)
-    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
-        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
-    if o is None:
-        o = torch.empty_like(q)
-    _require(o, "o", q.dtype)
+    B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
+        q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if max_seq_len is None:
-        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
-    max_blocks = block_table.shape[1]
     dt = _dtype_code(q.dtype)
-    eff_max = min(int(max_seq_len), max_blocks * page_size)
-    plan = paged_plan(B, H, Hkv, q.dtype, page_size, eff_max, int(total_kv), 0, opt)
+    eff_max = min(max_seq_len, max_blocks * page_size)
+    plan = paged_plan(B, H, Hkv, dt, page_size, eff_max, int(total_kv), 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
     _check(lib().fd_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                  seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
-                                 num_pages, max_blocks, int(max_seq_len), int(total_kv), dt, wp or None, wb,
+                                 num_pages, max_blocks, max_seq_len, int(total_kv), dt, wp or None, wb,
                                  _opt_ptr(opt), _stream_handle(stream)))
+    return o
+
+
+def fd_paged_decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, k_scale: float, v_scale: float, page_size: int | None = None,
+                          o: torch.Tensor | None = None, scale: float | None = None, max_seq_len: int | None = None,
+                          total_kv: int = 0, ws: torch.Tensor | None = None, opt: FdOptions | None = None,
+                          stream=None) -> torch.Tensor:
+    """Batched paged GQA decode over FP8 E4M3 caches (codes as float8_e4m3fn or uint8)
+    with per-tensor scales; otherwise as ``fd_paged_decode``."""
+    B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
+        q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, _fp8_cache_dtype(k_cache, "k_cache"))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = _fp8_code(q.dtype)
+    eff_max = min(max_seq_len, max_blocks * page_size)
+    plan = paged_plan(B, H, Hkv, dt, page_size, eff_max, int(total_kv), 0, opt)
+    wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    _check(lib().fd_paged_decode_fp8kv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                       seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), float(k_scale),
+                                       float(v_scale), B, H, Hkv, D, num_pages, max_blocks, max_seq_len,
+                                       int(total_kv), dt, wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
     return o
 
 

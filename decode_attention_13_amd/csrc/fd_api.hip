@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -77,7 +78,7 @@ int mfma_heads_per_group(int G) {
 // Matrix cores when a group of query heads forms a tile (16-bit inputs, >= 3
 // heads per KV head); the vector ALUs otherwise.
 int pick_kernel(fd_dtype dtype, int G, int forced) {
-    const bool mfma_ok = dtype != FD_DTYPE_F32 && mfma_heads_per_group(G) > 0;
+    const bool mfma_ok = fd::query_dtype(dtype) != FD_DTYPE_F32 && mfma_heads_per_group(G) > 0;
     if (forced == FD_KERNEL_VALU) return FD_KERNEL_VALU;
     if (forced == FD_KERNEL_MFMA) return mfma_ok ? FD_KERNEL_MFMA : -1;
     return (mfma_ok && G >= 3) ? FD_KERNEL_MFMA : FD_KERNEL_VALU;
@@ -87,7 +88,7 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
     if (B < 1 || H < 1 || Hkv < 1) return fail(FD_ERR_INVALID_ARG, "B, H and Hkv must be >= 1 (got %d, %d, %d)", B, H, Hkv);
     if (H % Hkv != 0) return fail(FD_ERR_INVALID_ARG, "H (%d) must be a multiple of Hkv (%d)", H, Hkv);
     if (D != FD_HEAD_DIM) return fail(FD_ERR_UNSUPPORTED, "head dim %d unsupported (only %d)", D, FD_HEAD_DIM);
-    if (dtype != FD_DTYPE_F32 && dtype != FD_DTYPE_F16 && dtype != FD_DTYPE_BF16)
+    if (dtype < FD_DTYPE_F32 || dtype > FD_DTYPE_BF16_KV_E4M3)
         return fail(FD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (opt) {
         if (opt->force_num_splits < 0 || opt->force_chunk < 0)
@@ -207,7 +208,7 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         m.ws_lse = a.ws_lse;
         m.chunk = plan.chunk;
         m.num_splits = plan.num_splits;
-        e = fd::launch_merge(dtype, paged, B, m, stream);
+        e = fd::launch_merge(fd::query_dtype(dtype), paged, B, m, stream);
         if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "merge kernel launch: %s", hipGetErrorString(e));
     }
     return FD_OK;
@@ -253,8 +254,19 @@ fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_s
     return make_plan(B, H, Hkv, dtype, max_seq_len, total, page_size, num_cus, opt, out);
 }
 
-fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
-                    fd_dtype dtype, float scale, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+}  // extern "C"
+
+namespace {
+
+fd_status check_scales(float k_scale, float v_scale) {
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(FD_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    return FD_OK;
+}
+
+fd_status decode_impl(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
+                      fd_dtype dtype, float scale, float k_scale, float v_scale, void *ws, size_t ws_bytes,
+                      const fd_options *opt, void *stream) {
     fd_status s = check_common(1, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
     if (S < 0) return fail(FD_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
@@ -273,7 +285,8 @@ fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H,
     a.Hkv = Hkv;
     a.G = H / Hkv;
     a.max_len = S;
-    a.scale_log2 = scale * fd::kLog2eHost;
+    a.scale_log2 = scale * k_scale * fd::kLog2eHost;
+    a.v_scale = v_scale;
     fd::MergeArgs m{};
     m.out = o;
     m.H = H;
@@ -281,10 +294,10 @@ fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H,
     return run(plan, dtype, false, a, m, 1, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream));
 }
 
-fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
-                          const int32_t *seq_lens, int page_size, void *o, float scale, int B, int H, int Hkv, int D,
-                          int num_pages, int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
-                          void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+fd_status paged_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
+                     const int32_t *seq_lens, int page_size, void *o, float scale, float k_scale, float v_scale,
+                     int B, int H, int Hkv, int D, int num_pages, int max_blocks, int max_seq_len, long long total_kv,
+                     fd_dtype dtype, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
     fd_status s = check_common(B, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
@@ -318,13 +331,56 @@ fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cach
     a.page_shift = shift;
     a.max_blocks = max_blocks;
     a.num_pages = num_pages;
-    a.scale_log2 = scale * fd::kLog2eHost;
+    a.scale_log2 = scale * k_scale * fd::kLog2eHost;
+    a.v_scale = v_scale;
     fd::MergeArgs m{};
     m.seq_lens = seq_lens;
     m.out = o;
     m.H = H;
     m.max_len = eff_max;
     return run(plan, dtype, true, a, m, B, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
+                    fd_dtype dtype, float scale, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+    if (fd::is_fp8_cache(dtype)) return fail(FD_ERR_UNSUPPORTED, "FP8 KV caches go through fd_decode_fp8kv");
+    return decode_impl(q, k, v, o, H, Hkv, S, D, dtype, scale, 1.f, 1.f, ws, ws_bytes, opt, stream);
+}
+
+fd_status fd_decode_fp8kv(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
+                          fd_dtype dtype, float scale, float k_scale, float v_scale, void *ws, size_t ws_bytes,
+                          const fd_options *opt, void *stream) {
+    if (!fd::is_fp8_cache(dtype))
+        return fail(FD_ERR_UNSUPPORTED, "fd_decode_fp8kv takes FD_DTYPE_F16_KV_E4M3 or FD_DTYPE_BF16_KV_E4M3");
+    fd_status s = check_scales(k_scale, v_scale);
+    if (s != FD_OK) return s;
+    return decode_impl(q, k, v, o, H, Hkv, S, D, dtype, scale, k_scale, v_scale, ws, ws_bytes, opt, stream);
+}
+
+fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
+                          const int32_t *seq_lens, int page_size, void *o, float scale, int B, int H, int Hkv, int D,
+                          int num_pages, int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
+                          void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+    if (fd::is_fp8_cache(dtype)) return fail(FD_ERR_UNSUPPORTED, "FP8 KV caches go through fd_paged_decode_fp8kv");
+    return paged_impl(q, k_cache, v_cache, block_table, seq_lens, page_size, o, scale, 1.f, 1.f, B, H, Hkv, D,
+                      num_pages, max_blocks, max_seq_len, total_kv, dtype, ws, ws_bytes, opt, stream);
+}
+
+fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
+                                const int32_t *seq_lens, int page_size, void *o, float scale, float k_scale,
+                                float v_scale, int B, int H, int Hkv, int D, int num_pages, int max_blocks,
+                                int max_seq_len, long long total_kv, fd_dtype dtype, void *ws, size_t ws_bytes,
+                                const fd_options *opt, void *stream) {
+    if (!fd::is_fp8_cache(dtype))
+        return fail(FD_ERR_UNSUPPORTED, "fd_paged_decode_fp8kv takes FD_DTYPE_F16_KV_E4M3 or FD_DTYPE_BF16_KV_E4M3");
+    fd_status s = check_scales(k_scale, v_scale);
+    if (s != FD_OK) return s;
+    return paged_impl(q, k_cache, v_cache, block_table, seq_lens, page_size, o, scale, k_scale, v_scale, B, H, Hkv,
+                      D, num_pages, max_blocks, max_seq_len, total_kv, dtype, ws, ws_bytes, opt, stream);
 }
 
 const char *fd_status_string(fd_status s) {

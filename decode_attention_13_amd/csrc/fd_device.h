@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fd_internal.h"
 
 namespace fd {
@@ -206,6 +208,78 @@ template <typename T>
 __device__ __forceinline__ uint4 load_stream16_at(const T *base, size_t byte_off) {
     return load_stream16(reinterpret_cast<const char *>(base) + byte_off);
 }
+
+// ---------------------------------------------------------------- KV rows
+// Cache element types and how a 16-lane row group reads one 128-element K/V
+// row: lane c owns 8 elements. Raw is what one lane loads per row piece.
+//   bf16/f16: elements [8c, 8c+8), one 16-byte load.
+//   fp32:     elements [4c, 4c+4) and [64+4c, 64+4c+4), two 16-byte loads.
+//   FP8 E4M3: elements [8c, 8c+8), one 8-byte load; codes are converted to fp32
+//             in registers (v_cvt_pk_f32_fp8, OCP E4M3 on gfx950), which is exact.
+struct fp8e4m3 {
+    unsigned char bits;
+};
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename KV>
+struct KvRow;
+
+template <>
+struct KvRow<float> {
+    typedef uint4 Raw;
+    static constexpr int kPieces = 2;
+    __device__ static int offset(int c, int piece) { return piece * 64 + 4 * c; }
+    __device__ static int index(int c, int e) { return (e >> 2) * 64 + 4 * c + (e & 3); }
+    __device__ static Raw load(const char *p) { return load_stream16(p); }
+    __device__ static void unpack(const Raw *x, float *f) { Elem<float>::unpack(x, f); }
+};
+
+template <>
+struct KvRow<__bf16> {
+    typedef uint4 Raw;
+    static constexpr int kPieces = 1;
+    __device__ static int offset(int c, int) { return 8 * c; }
+    __device__ static int index(int c, int e) { return 8 * c + e; }
+    __device__ static Raw load(const char *p) { return load_stream16(p); }
+    __device__ static void unpack(const Raw *x, float *f) { Elem<__bf16>::unpack(x, f); }
+};
+
+template <>
+struct KvRow<_Float16> {
+    typedef uint4 Raw;
+    static constexpr int kPieces = 1;
+    __device__ static int offset(int c, int) { return 8 * c; }
+    __device__ static int index(int c, int e) { return 8 * c + e; }
+    __device__ static Raw load(const char *p) { return load_stream16(p); }
+    __device__ static void unpack(const Raw *x, float *f) { Elem<_Float16>::unpack(x, f); }
+};
+
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+}
+
+template <>
+struct KvRow<fp8e4m3> {
+    typedef uint2 Raw;
+    static constexpr int kPieces = 1;
+    __device__ static int offset(int c, int) { return 8 * c; }
+    __device__ static int index(int c, int e) { return 8 * c + e; }
+    __device__ static Raw load(const char *p) {
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        return make_uint2(x.x, x.y);
+    }
+    __device__ static void unpack(const Raw *x, float *f) {
+        e4m3x4_to_f32(x->x, f);
+        e4m3x4_to_f32(x->y, f + 4);
+    }
+};
 
 // ---------------------------------------------------------------- softmax state
 // Online-softmax state in the log2 domain: running max m (of scale*log2(e)*s),

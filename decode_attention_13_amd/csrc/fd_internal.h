@@ -38,8 +38,18 @@ struct SplitArgs {
     int page_shift;         // log2(page_size)
     int max_blocks;
     int num_pages;
-    float scale_log2;       // scale * log2(e)
+    float scale_log2;       // scale * k_scale * log2(e)
+    float v_scale;          // dequantisation scale of V (1 unless the cache is FP8)
 };
+
+// Query/output dtype of a call (FP8-cache codes map to their query type).
+inline fd_dtype query_dtype(fd_dtype d) {
+    if (d == FD_DTYPE_F16_KV_E4M3) return FD_DTYPE_F16;
+    if (d == FD_DTYPE_BF16_KV_E4M3) return FD_DTYPE_BF16;
+    return d;
+}
+
+inline bool is_fp8_cache(fd_dtype d) { return d == FD_DTYPE_F16_KV_E4M3 || d == FD_DTYPE_BF16_KV_E4M3; }
 
 struct MergeArgs {
     const float *ws_o;

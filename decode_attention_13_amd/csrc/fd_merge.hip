@@ -89,6 +89,7 @@ hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, h
         case FD_DTYPE_F32: return paged ? launch_one<float, true>(B, a, st) : launch_one<float, false>(B, a, st);
         case FD_DTYPE_F16: return paged ? launch_one<_Float16, true>(B, a, st) : launch_one<_Float16, false>(B, a, st);
         case FD_DTYPE_BF16: return paged ? launch_one<__bf16, true>(B, a, st) : launch_one<__bf16, false>(B, a, st);
+        default: break;  // callers pass the query dtype
     }
     return hipErrorInvalidValue;
 }

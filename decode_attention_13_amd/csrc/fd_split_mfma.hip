@@ -26,6 +26,12 @@
 // The wave's next tile of K and V is loaded into registers while the current
 // one is computed. The four waves' states are merged once at the end through
 // LDS.
+//
+// FP8 E4M3 caches: K and V codes are converted to the query type in registers
+// (v_cvt_scalef32_pk_{bf16,f16}_fp8 with unit scale; every E4M3 value is exact
+// in bf16 and in f16) and the same 16-bit MFMAs run. The per-tensor scales are
+// applied in fp32: k_scale inside the folded softmax scale, v_scale on the
+// normalised output.
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -42,7 +48,6 @@ constexpr int kMaxHeads = 16;            // MFMA tile columns
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -64,6 +69,10 @@ struct Mfma<__bf16> {
     }
     __device__ static float lo_of(uint32_t w) { return bf16_lo(w); }
     __device__ static float hi_of(uint32_t w) { return bf16_hi(w); }
+    template <bool HI>  // E4M3 codes in bytes 2*HI, 2*HI+1 of w -> two bf16
+    __device__ static uint32_t from_e4m3(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
 };
 
 template <>
@@ -77,12 +86,71 @@ struct Mfma<_Float16> {
     }
     __device__ static float lo_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
     __device__ static float hi_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+    template <bool HI>
+    __device__ static uint32_t from_e4m3(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    }
 };
 
-template <typename T, int MODE>
+// How one lane holds its share of K and V for query type T and cache type KV.
+//   K: lane (g, c) holds, for token c of a 16-token block, the 32 head-dim
+//      slots of its group; kk-th MFMA operand = 8 of them. Q uses the same
+//      slot order (q_slot).
+//   V: lane c of group g loads the elements [8c, 8c+8) of one row; v_lds
+//      gives them as 8 values of T for the LDS copy.
+template <typename T, typename KV>
+struct KvFrag {  // 16-bit cache of the query type
+    static constexpr int kKRegs = 4;  // uint4 per lane and 16-token block
+    typedef uint4 VRaw;
+    // slot d = kk*32 + g*8 + j: the 4 lanes of a row read 64 contiguous bytes per load
+    __device__ static int q_slot(int g, int kk) { return kk * 32 + g * 8; }
+    template <typename Off>
+    __device__ static void load_k(const char *base, Off off, int g, uint4 (&kx)[kKRegs]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kx[kk] = load16(base + off + g * 16 + kk * 64);
+    }
+    __device__ static uint4 k_operand(const uint4 (&kx)[kKRegs], int kk) { return kx[kk]; }
+    template <typename Off>
+    __device__ static VRaw load_v(const char *base, Off off, int c) {
+        return load_stream16(base + off + c * 16);
+    }
+    __device__ static u32x4 v_lds(VRaw v) { return u32x4{v.x, v.y, v.z, v.w}; }
+};
+
+template <typename T>
+struct KvFrag<T, fp8e4m3> {
+    static constexpr int kKRegs = 2;
+    typedef u32x2 VRaw;
+    // slot d = (kk/2)*64 + g*16 + (kk%2)*8 + j: one 16-byte load per half row,
+    // again 64 contiguous bytes per row and load
+    __device__ static int q_slot(int g, int kk) { return (kk >> 1) * 64 + g * 16 + (kk & 1) * 8; }
+    template <typename Off>
+    __device__ static void load_k(const char *base, Off off, int g, uint4 (&kx)[kKRegs]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) kx[h] = load16(base + off + g * 16 + h * 64);
+    }
+    __device__ static uint4 k_operand(const uint4 (&kx)[kKRegs], int kk) {
+        const uint32_t w0 = (kk & 1) ? kx[kk >> 1].z : kx[kk >> 1].x;
+        const uint32_t w1 = (kk & 1) ? kx[kk >> 1].w : kx[kk >> 1].y;
+        return make_uint4(Mfma<T>::template from_e4m3<false>(w0), Mfma<T>::template from_e4m3<true>(w0),
+                          Mfma<T>::template from_e4m3<false>(w1), Mfma<T>::template from_e4m3<true>(w1));
+    }
+    template <typename Off>
+    __device__ static VRaw load_v(const char *base, Off off, int c) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(base + off + c * 8));
+    }
+    __device__ static u32x4 v_lds(VRaw v) {
+        return u32x4{Mfma<T>::template from_e4m3<false>(v.x), Mfma<T>::template from_e4m3<true>(v.x),
+                     Mfma<T>::template from_e4m3<false>(v.y), Mfma<T>::template from_e4m3<true>(v.y)};
+    }
+};
+
+template <typename T, typename KV, int MODE>
 __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
+    using F = KvFrag<T, KV>;
+    constexpr int KR = F::kKRegs;
     using E = Elem<T>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -113,18 +181,18 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     }
     const int t_end = min(t_begin + a.chunk, L);
 
-    const T *kbase = reinterpret_cast<const T *>(a.k);
-    const T *vbase = reinterpret_cast<const T *>(a.v);
-    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(T),
-                   (size_t)kvh * kHeadDim * sizeof(T)};
+    const char *kbase = reinterpret_cast<const char *>(a.k);
+    const char *vbase = reinterpret_cast<const char *>(a.v);
+    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(KV),
+                   (size_t)kvh * kHeadDim * sizeof(KV)};
 
-    // B operand of S: q[h0 + c][kk*32 + g*8 .. +8], zero for padded heads.
+    // B operand of S: 8 head-dim slots of q[h0 + c] per kk, zero for padded heads.
     uint4 qb[4];
     {
         const T *qrow = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.H + h0 + min(c, nh - 1)) * kHeadDim;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            qb[kk] = load16(qrow + kk * 32 + g * 8);
+            qb[kk] = load16(qrow + F::q_slot(g, kk));
             if (c >= nh) qb[kk] = make_uint4(0, 0, 0, 0);
         }
     }
@@ -143,25 +211,20 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     // A tile is two 16-token blocks. When the second block holds no valid token
     // its rows are clamped into the first, so both are addressed from block 0.
     auto block_start = [&](int t0, int h) { return (h == 0 || t0 + 16 < t_end) ? t0 + 16 * h : t0; };
-    auto load_k = [&](int j, uint4 (&kx)[2][4]) {
+    auto load_k = [&](int j, uint4 (&kx)[2][KR]) {
         const int t0 = t_begin + j * kTile;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int tok = min(t0 + sb * 16 + c, t_end - 1);
             if constexpr (MODE == kPagedRow) {
-                const size_t off = A.row(tok) + (size_t)g * 16;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) kx[sb][kk] = load16(reinterpret_cast<const char *>(kbase) + off + kk * 64);
+                F::load_k(kbase, A.row(tok), g, kx[sb]);
             } else {
                 const int B = block_start(t0, sb);
-                const T *kb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(kbase) + A.block(B));
-                const uint32_t off = (uint32_t)(tok - B) * (uint32_t)A.token_bytes + g * 16;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) kx[sb][kk] = load16(reinterpret_cast<const char *>(kb) + off + kk * 64);
+                F::load_k(kbase + A.block(B), (uint32_t)(tok - B) * (uint32_t)A.token_bytes, g, kx[sb]);
             }
         }
     };
-    auto load_v = [&](int j, uint4 (&vx)[8]) {
+    auto load_v = [&](int j, typename F::VRaw (&vx)[8]) {
         const int t0 = t_begin + j * kTile;
         size_t base[2] = {0, 0};
         if constexpr (MODE != kPagedRow) {
@@ -172,11 +235,10 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
         for (int i = 0; i < 8; ++i) {
             const int tok = min(t0 + 4 * i + g, t_end - 1);
             if constexpr (MODE == kPagedRow) {
-                vx[i] = load_stream16_at(vbase, A.row(tok) + c * 16);
+                vx[i] = F::load_v(vbase, A.row(tok), c);
             } else {
                 const int h = i >> 2;
-                const T *vb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(vbase) + base[h]);
-                vx[i] = load_stream16_at(vb, (uint32_t)(tok - block_start(t0, h)) * (uint32_t)A.token_bytes + c * 16);
+                vx[i] = F::load_v(vbase + base[h], (uint32_t)(tok - block_start(t0, h)) * (uint32_t)A.token_bytes, c);
             }
         }
     };
@@ -184,14 +246,15 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     // K: one register set, refilled with the wave's next tile as soon as the S
     // MFMAs have consumed it. V: two register sets used as a ring, so the V rows
     // of the next two tiles are in flight while this tile is computed.
-    uint4 kx[2][4], vA[8], vB[8];
-    auto tile = [&](int j, uint4 (&vcur)[8]) {
+    uint4 kx[2][KR];
+    typename F::VRaw vA[8], vB[8];
+    auto tile = [&](int j, typename F::VRaw (&vcur)[8]) {
         const int t0 = t_begin + j * kTile;
         // V tile -> LDS (row r = token t0 + r, padded rows), then refill the set
         // with the tile after next.
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *(lds_u32x4 *)(vreg + (4 * i + g) * kRowPad + c * 16) = u32x4{vcur[i].x, vcur[i].y, vcur[i].z, vcur[i].w};
+            *(lds_u32x4 *)(vreg + (4 * i + g) * kRowPad + c * 16) = F::v_lds(vcur[i]);
         if (j + 2 * kWaves < ntiles) load_v(j + 2 * kWaves, vcur);
         // S^T tiles: s[sb][i] = score of token t0 + sb*16 + g*4 + i for head c
         f32x4 s[2];
@@ -199,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
         for (int sb = 0; sb < 2; ++sb) {
             s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) s[sb] = M::mma(kx[sb][kk], qb[kk], s[sb]);
+            for (int kk = 0; kk < 4; ++kk) s[sb] = M::mma(F::k_operand(kx[sb], kk), qb[kk], s[sb]);
         }
         if (j + kWaves < ntiles) load_k(j + kWaves, kx);
         float x[8];
@@ -305,24 +368,24 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
             o = __builtin_fmaf(wgt, s_acc[(w * kMaxHeads + hh) * kHeadDim + d], o);
         }
         lse = (Mx + log2_fast(l)) * kLn2;
-        return o / l;
+        return a.v_scale * (o / l);
     });
 }
 
-template <typename T, int MODE>
+template <typename T, typename KV, int MODE>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, MODE>), s, args, st, e0, e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, KV, MODE>), s, args, st, e0, e1);
 }
 
-template <typename T>
+template <typename T, typename KV>
 hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_one<T, kContig>(s, a, st, e0, e1);
-        case kPagedBlock: return launch_one<T, kPagedBlock>(s, a, st, e0, e1);
-        case kPagedRow: return launch_one<T, kPagedRow>(s, a, st, e0, e1);
+        case kContig: return launch_one<T, KV, kContig>(s, a, st, e0, e1);
+        case kPagedBlock: return launch_one<T, KV, kPagedBlock>(s, a, st, e0, e1);
+        case kPagedRow: return launch_one<T, KV, kPagedRow>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -333,8 +396,10 @@ hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape
                              hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if (gt < 1 || gt > kMaxHeads) return hipErrorInvalidValue;
     switch (dtype) {
-        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

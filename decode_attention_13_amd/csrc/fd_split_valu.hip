@@ -10,7 +10,12 @@
 // set before computing the current one (a register double buffer; no LDS is
 // needed because every lane consumes exactly the bytes it loaded).
 //
-// Per row: q.k on v_dot2 (16-bit) or FMA (fp32) over the lane's 8 elements,
+// The cache element type KV may differ from the query/output type T: an FP8
+// E4M3 cache (8-byte loads, codes converted to fp32 in registers) is read with
+// f16/bf16 queries; its per-tensor scales are folded into the score scale
+// (k_scale) and the stored output (v_scale).
+//
+// Per row: q.k on v_dot2 (16-bit) or FMA (fp32, FP8) over the lane's 8 elements,
 // a 4-step DPP butterfly across the row, then the online-softmax update in
 // the log2 domain ("FlashAttention 与推理算子", section "FlashAttention：分块 +
 // online softmax"; the exp2 form with scale*log2(e) folded into the scores as
@@ -31,11 +36,15 @@ constexpr int kRows = 4;               // rows per 16-lane group per wave tile
 constexpr int kWaveTile = 4 * kRows;   // tokens per wave tile
 constexpr int kWaves = kThreads / 64;
 
-template <typename T, int GT, int MODE>
+template <typename T, typename KV, int GT, int MODE>
 __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     constexpr bool PAGED = MODE != kContig;
     using E = Elem<T>;
-    constexpr int NL = E::kLoads;
+    using R = KvRow<KV>;
+    using Raw = typename R::Raw;
+    constexpr int NL = R::kPieces;
+    // Packed 16-bit q.k on v_dot2 when the cache holds the query's own type.
+    constexpr bool kPackedDot = std::is_same<T, KV>::value && !std::is_same<T, float>::value;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;
@@ -63,27 +72,28 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     }
     const int t_end = min(t_begin + a.chunk, L);
 
-    const T *kbase = reinterpret_cast<const T *>(a.k);
-    const T *vbase = reinterpret_cast<const T *>(a.v);
-    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(T),
-                   (size_t)kvh * kHeadDim * sizeof(T)};
+    const char *kbase = reinterpret_cast<const char *>(a.k);
+    const char *vbase = reinterpret_cast<const char *>(a.v);
+    KvAddr<MODE> A{s_pages, page_first, a.page_shift, a.Hkv * kHeadDim * (int)sizeof(KV),
+                   (size_t)kvh * kHeadDim * sizeof(KV)};
 
-    // q fragments of the GT heads: fp32 for fp32 inputs, packed pairs otherwise.
+    // q fragments of the GT heads, on the lane's elements R::index(c, e):
+    // packed pairs for the v_dot2 path, fp32 otherwise.
     float qf[GT][8];
     uint32_t qp[GT][4];
     const T *qbase = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.H + h0) * kHeadDim;
 #pragma unroll
     for (int gi = 0; gi < GT; ++gi) {
-        uint4 x[NL];
+        uint4 x[E::kLoads];
 #pragma unroll
-        for (int pc = 0; pc < NL; ++pc) x[pc] = load16(qbase + gi * kHeadDim + E::offset(c, pc));
-        if constexpr (NL == 2) {
-            E::unpack(x, qf[gi]);
-        } else {
+        for (int pc = 0; pc < E::kLoads; ++pc) x[pc] = load16(qbase + gi * kHeadDim + E::offset(c, pc));
+        if constexpr (kPackedDot) {
             qp[gi][0] = x[0].x;
             qp[gi][1] = x[0].y;
             qp[gi][2] = x[0].z;
             qp[gi][3] = x[0].w;
+        } else {
+            E::unpack(x, qf[gi]);
         }
     }
 
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 
     // Tile j covers the 16-aligned block [tb, tb + 16), tb = t_begin + 16 j; rows past
     // t_end re-read the last valid row and are masked.
-    auto load_tile = [&](int j, uint4 (&kx)[kRows][NL], uint4 (&vx)[kRows][NL]) {
+    auto load_tile = [&](int j, Raw (&kx)[kRows][NL], Raw (&vx)[kRows][NL]) {
         const int tb = t_begin + j * kWaveTile;
         const int t0 = tb + grp * kRows;
         if constexpr (MODE == kPagedRow) {
@@ -109,27 +119,40 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
                 const size_t off = A.row(min(t0 + r, t_end - 1));
 #pragma unroll
                 for (int pc = 0; pc < NL; ++pc) {
-                    kx[r][pc] = load_stream16_at(kbase, off + E::offset(c, pc) * sizeof(T));
-                    vx[r][pc] = load_stream16_at(vbase, off + E::offset(c, pc) * sizeof(T));
+                    kx[r][pc] = R::load(kbase + off + R::offset(c, pc) * sizeof(KV));
+                    vx[r][pc] = R::load(vbase + off + R::offset(c, pc) * sizeof(KV));
                 }
             }
         } else {
             const size_t base = A.block(tb);
-            const T *kb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(kbase) + base);
-            const T *vb = reinterpret_cast<const T *>(reinterpret_cast<const char *>(vbase) + base);
+            const char *kb = kbase + base;
+            const char *vb = vbase + base;
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
                 const uint32_t off = (uint32_t)(min(t0 + r, t_end - 1) - tb) * (uint32_t)A.token_bytes;
 #pragma unroll
                 for (int pc = 0; pc < NL; ++pc) {
-                    kx[r][pc] = load_stream16_at(kb, off + E::offset(c, pc) * sizeof(T));
-                    vx[r][pc] = load_stream16_at(vb, off + E::offset(c, pc) * sizeof(T));
+                    kx[r][pc] = R::load(kb + off + R::offset(c, pc) * sizeof(KV));
+                    vx[r][pc] = R::load(vb + off + R::offset(c, pc) * sizeof(KV));
                 }
             }
         }
     };
 
-    auto compute_tile = [&](int j, const uint4 (&kx)[kRows][NL], const uint4 (&vx)[kRows][NL]) {
+    auto dot = [&](int gi, const Raw *kr) -> float {
+        if constexpr (kPackedDot) {
+            return E::dot(qf[gi], qp[gi], reinterpret_cast<const uint4 *>(kr));
+        } else {
+            float kf[8];
+            R::unpack(kr, kf);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qf[gi][e], kf[e], s);
+            return s;
+        }
+    };
+
+    auto compute_tile = [&](int j, const Raw (&kx)[kRows][NL], const Raw (&vx)[kRows][NL]) {
         const int t0 = t_begin + j * kWaveTile + grp * kRows;
         float p[GT][kRows];
 #pragma unroll
@@ -137,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             const bool valid = t0 + r < t_end;
 #pragma unroll
             for (int gi = 0; gi < GT; ++gi) {
-                const float d = row16_sum(E::dot(qf[gi], qp[gi], kx[r]));
+                const float d = row16_sum(dot(gi, kx[r]));
                 p[gi][r] = valid ? d * a.scale_log2 : -INFINITY;
             }
         }
@@ -162,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             float vf[8];
-            E::unpack(vx[r], vf);
+            R::unpack(vx[r], vf);
 #pragma unroll
             for (int gi = 0; gi < GT; ++gi)
 #pragma unroll
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
         }
     };
 
-    uint4 kA[kRows][NL], vA[kRows][NL], kB[kRows][NL], vB[kRows][NL];
+    Raw kA[kRows][NL], vA[kRows][NL], kB[kRows][NL], vB[kRows][NL];
     int j = wave;
     if (j < ntiles) load_tile(j, kA, vA);
     while (j < ntiles) {
@@ -208,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 #pragma unroll
         for (int gi = 0; gi < GT; ++gi) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][gi][E::index(c, e)] = acc[gi][e];
+            for (int e = 0; e < 8; ++e) s_acc[wave][gi][R::index(c, e)] = acc[gi][e];
             if (c == 0) {
                 s_m[wave][gi] = m[gi];
                 s_l[wave][gi] = l[gi];
@@ -232,35 +255,35 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             o = __builtin_fmaf(wgt, s_acc[w][gi][d], o);
         }
         lse = (M + log2_fast(lsum)) * kLn2;
-        return o / lsum;
+        return a.v_scale * (o / lsum);
     });
 }
 
-template <typename T, int GT, int MODE>
+template <typename T, typename KV, int GT, int MODE>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, GT, MODE>), s, args, st, e0, e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, KV, GT, MODE>), s, args, st, e0, e1);
 }
 
-template <typename T, int MODE>
+template <typename T, typename KV, int MODE>
 hipError_t launch_gt(int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (gt) {
-        case 1: return launch_one<T, 1, MODE>(s, a, st, e0, e1);
-        case 2: return launch_one<T, 2, MODE>(s, a, st, e0, e1);
-        case 4: return launch_one<T, 4, MODE>(s, a, st, e0, e1);
-        case 8: return launch_one<T, 8, MODE>(s, a, st, e0, e1);
+        case 1: return launch_one<T, KV, 1, MODE>(s, a, st, e0, e1);
+        case 2: return launch_one<T, KV, 2, MODE>(s, a, st, e0, e1);
+        case 4: return launch_one<T, KV, 4, MODE>(s, a, st, e0, e1);
+        case 8: return launch_one<T, KV, 8, MODE>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename T, typename KV>
 hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_gt<T, kContig>(gt, s, a, st, e0, e1);
-        case kPagedBlock: return launch_gt<T, kPagedBlock>(gt, s, a, st, e0, e1);
-        case kPagedRow: return launch_gt<T, kPagedRow>(gt, s, a, st, e0, e1);
+        case kContig: return launch_gt<T, KV, kContig>(gt, s, a, st, e0, e1);
+        case kPagedBlock: return launch_gt<T, KV, kPagedBlock>(gt, s, a, st, e0, e1);
+        case kPagedRow: return launch_gt<T, KV, kPagedRow>(gt, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -270,9 +293,11 @@ hipError_t launch_mode(int mode, int gt, const LaunchShape &s, const SplitArgs &
 hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
                              hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (dtype) {
-        case FD_DTYPE_F32: return launch_mode<float>(mode, gt, s, a, st, e0, e1);
-        case FD_DTYPE_F16: return launch_mode<_Float16>(mode, gt, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_F32: return launch_mode<float, float>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, gt, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, gt, s, a, st, e0, e1);
     }
     return hipErrorInvalidValue;
 }

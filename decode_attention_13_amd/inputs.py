@@ -173,6 +173,32 @@ def paged_inputs(B: int, H: int, Hkv: int, D: int, dtype: str, page_size: int, s
             "total_kv": int(lens.astype(np.int64).sum()), "scale": default_scale(D)}
 
 
+# --------------------------------------------------------------------------- FP8 KV
+
+FP8_SCALE = 1.0 / 16.0  # per-tensor dequantisation scale of the synthetic FP8 caches
+
+
+def to_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """FP8 E4M3 codes of x / scale (round to nearest even, clamped to +-448)."""
+    return (x.float() / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+
+
+def with_fp8_kv(d: dict, scale: float = FP8_SCALE) -> dict:
+    """The same workload with its K/V (or caches) stored as E4M3 codes, q kept.
+
+    The codes quantise the original N(0,1) draws; ``k_scale``/``v_scale`` map
+    them back. NaN poison (used by the paging tests) stays NaN.
+    """
+    out = dict(d)
+    for key in ("k", "v", "k_cache", "v_cache"):
+        if key in d:
+            out[key] = to_e4m3(d[key], scale)
+    out["k_scale"] = scale
+    out["v_scale"] = scale
+    out["kv_dtype"] = "fp8"
+    return out
+
+
 # --------------------------------------------------------------------------- workloads
 
 

@@ -48,13 +48,18 @@ extern "C" {
 typedef enum fd_dtype {
     FD_DTYPE_F32 = 0,
     FD_DTYPE_F16 = 1,
-    FD_DTYPE_BF16 = 2
+    FD_DTYPE_BF16 = 2,
+    /* q and o in f16/bf16; K and V stored as OCP FP8 E4M3 codes (1 byte each)
+     * with per-tensor dequantisation scales: only for the *_fp8kv calls and
+     * their plans. */
+    FD_DTYPE_F16_KV_E4M3 = 3,
+    FD_DTYPE_BF16_KV_E4M3 = 4
 } fd_dtype;
 
 typedef enum fd_status {
     FD_OK = 0,
     FD_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, H % Hkv != 0, bad option */
-    FD_ERR_UNSUPPORTED = 2, /* D != 128, page_size not a power of two in [1, 1024], unknown dtype */
+    FD_ERR_UNSUPPORTED = 2, /* D != 128, page_size not a power of two in [1, 1024], dtype not valid for the call */
     FD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fd_plan.workspace_bytes */
     FD_ERR_DEVICE = 4,      /* no current HIP device / attribute query failed */
     FD_ERR_LAUNCH = 5       /* a kernel launch or event record returned an error */
@@ -166,6 +171,33 @@ fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cach
                           void *o, float scale, int B, int H, int Hkv, int D, int num_pages,
                           int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
                           void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
+
+/*
+ * FP8 KV cache. "FlashAttention 与推理算子", in the improvements listed after its
+ * paged GQA kernel, notes that a real KV cache is BF16 or FP8, read with
+ * 128-bit loads and converted to FP32 in registers. Here every K and V element
+ * is an OCP FP8 E4M3 code (bias 7, 3 mantissa bits, no infinities, max 448)
+ * and the cached value is code x k_scale (K) or code x v_scale (V).
+ * Arguments as in fd_decode / fd_paged_decode, except:
+ *   k, v / k_cache, v_cache   E4M3 codes, same shapes, 1 byte per element
+ *                             (16-byte aligned as before)
+ *   dtype                     FD_DTYPE_F16_KV_E4M3 or FD_DTYPE_BF16_KV_E4M3:
+ *                             q and o are f16 / bf16
+ *   k_scale, v_scale          finite dequantisation scales of K and V
+ * The codes are converted exactly (to fp32 or, on the matrix cores, to the
+ * query type) and accumulated in fp32.
+ */
+fd_status fd_decode_fp8kv(const void *q, const void *k, const void *v, void *o,
+                          int H, int Hkv, int S, int D, fd_dtype dtype, float scale,
+                          float k_scale, float v_scale,
+                          void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
+
+fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *seq_lens, int page_size,
+                                void *o, float scale, float k_scale, float v_scale,
+                                int B, int H, int Hkv, int D, int num_pages,
+                                int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
+                                void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
 
 /* Static name of a status code. */
 const char *fd_status_string(fd_status s);

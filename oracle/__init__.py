@@ -13,6 +13,8 @@ Contents
 ``loops``   -- pure-Python three-pass and online-softmax recurrences for tiny
                inputs, used to pin ``decode`` against the pages' step-by-step
                algorithms.
+``fp8``     -- values of an FP8 E4M3 KV cache with per-tensor scales, and the
+               plain definition over them (contiguous and paged).
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (the pages' worked example, closed forms, a library routine,
@@ -34,3 +36,9 @@ from .decode import (  # noqa: F401
     merge_m_l,
 )
 from . import loops  # noqa: F401
+from .fp8 import (  # noqa: F401
+    dequantize_e4m3,
+    e4m3_value,
+    decode_attention_e4m3,
+    paged_decode_attention_e4m3,
+)

@@ -23,8 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("fd_decode", "fd_paged_decode", "fd_decode_plan", "fd_paged_plan", "fd_status_string",
-                     "fd_last_error", "fd_device_num_cus"):
+    for required in ("fd_decode", "fd_paged_decode", "fd_decode_fp8kv", "fd_paged_decode_fp8kv", "fd_decode_plan",
+                     "fd_paged_plan", "fd_status_string", "fd_last_error", "fd_device_num_cus"):
         assert required in names
 
 
@@ -134,6 +134,35 @@ def test_decode_rejects_bad_pointers_without_a_device():
     assert lib.fd_status_string(rc).decode() == "FD_ERR_UNSUPPORTED"
     rc = lib.fd_paged_decode(16, 16, 16, 18, 16, 16, 16, 0.1, 2, 8, 8, 128, 4, 4, 64, 0, 2, None, 0, None, None)
     assert lib.fd_status_string(rc).decode() == "FD_ERR_INVALID_ARG"  # misaligned block table
+
+
+def test_fp8_cache_plans_and_dtype_routing():
+    # E4M3 caches plan like their query type: same kernel choice and split shape
+    for q_name, code in (("f16", 3), ("bf16", 4)):
+        for H, Hkv in ((32, 32), (32, 4), (64, 8), (8, 1)):
+            a = fd.decode_plan(H, Hkv, 4096, q_name, 256)
+            b = fd.decode_plan(H, Hkv, 4096, code, 256)
+            assert a == b
+        a = fd.paged_plan(64, 32, 8, q_name, 16, 8192, 300000, 256)
+        b = fd.paged_plan(64, 32, 8, f"{q_name}_kv_e4m3", 16, 8192, 300000, 256)
+        assert a == b
+    lib = fd.lib()
+    # fd_decode refuses E4M3 codes; fd_decode_fp8kv refuses everything else
+    assert lib.fd_decode(16, 16, 16, 32, 8, 8, 512, 128, 3, 0.1, None, 0, None, None) == 2
+    for code in (0, 1, 2, 5):
+        assert lib.fd_decode_fp8kv(16, 16, 16, 32, 8, 8, 512, 128, code, 0.1, 1.0, 1.0, None, 0, None, None) == 2
+    assert lib.fd_paged_decode(16, 16, 16, 16, 16, 16, 16, 0.1, 2, 8, 8, 128, 4, 4, 64, 0, 4, None, 0, None,
+                               None) == 2
+    assert lib.fd_paged_decode_fp8kv(16, 16, 16, 16, 16, 16, 16, 0.1, 1.0, 1.0, 2, 8, 8, 128, 4, 4, 64, 0, 2, None,
+                                     0, None, None) == 2
+    # the scales must be finite
+    for ks, vs in ((float("inf"), 1.0), (1.0, float("nan"))):
+        assert lib.fd_decode_fp8kv(16, 16, 16, 32, 8, 8, 512, 128, 4, 0.1, ks, vs, None, 0, None, None) == 1
+        assert lib.fd_paged_decode_fp8kv(16, 16, 16, 16, 16, 16, 16, 0.1, ks, vs, 2, 8, 8, 128, 4, 4, 64, 0, 4, None,
+                                         0, None, None) == 1
+    # the binding refuses an FP8 cache for f32 queries before calling in
+    with pytest.raises(TypeError):
+        binding._fp8_code(torch.float32)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")

@@ -280,10 +280,52 @@ def pin_paged_equals_contiguous() -> bool:
     return bool(ok)
 
 
+def pin_e4m3_decoding() -> bool:
+    """Every E4M3 code against torch's float8_e4m3fn decoding (a library routine), plus
+    the format's landmarks: 1.0, the largest finite 448, the smallest subnormal 2^-9."""
+    import torch
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    table = oracle.dequantize_e4m3(np.arange(256, dtype=np.uint8), 1.0)
+    ok = np.array_equal(np.isnan(lib), np.isnan(table))
+    ok &= np.array_equal(lib[~np.isnan(lib)], table[~np.isnan(table)])
+    ok &= table[0x38] == 1.0 and table[0x7E] == 448.0 and table[0x01] == 2.0 ** -9 and table[0xB8] == -1.0
+    ok &= np.array_equal(oracle.dequantize_e4m3(np.array([0x38, 0x40], dtype=np.uint8), 0.0625), [0.0625, 0.125])
+    return bool(ok)
+
+
+def pin_e4m3_attention() -> bool:
+    """FP8 attention == the plain definition on the same values written out by hand: K
+    holds k_scale * {0, 1, 2, 3}, V holds v_scale * {-1, 1.5, 448} (all exact E4M3 values;
+    codes by torch's float8 encoder), with k_scale != v_scale; and the paged form over a
+    shuffled two-page table equals the contiguous one."""
+    import torch
+    ks, vs = 0.25, 3.0
+    kvals = np.array([[0.0, 1.0], [2.0, 3.0], [1.0, 0.0]])          # [S=3, D=2]
+    vvals = np.array([[-1.0, 1.5], [448.0, -1.0], [1.5, 1.5]])
+    codes = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q = np.array([[0.5, -1.0], [2.0, 0.25]])
+    o, lse = oracle.decode_attention_e4m3(q, codes(kvals)[:, None], codes(vvals)[:, None], ks, vs, 0.7)
+    s = 0.7 * (q @ (ks * kvals).T)                                  # [H, S], written out
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    want = (w / w.sum(axis=1, keepdims=True)) @ (vs * vvals)
+    ok = np.allclose(o, want, rtol=1e-13, atol=0) and np.allclose(lse, np.log(np.exp(s).sum(axis=1)), rtol=1e-13)
+    kc = np.zeros((2, 2, 1, 2), np.uint8)
+    vc = np.zeros((2, 2, 1, 2), np.uint8)
+    kc[1, 0, 0], kc[1, 1, 0], kc[0, 0, 0] = codes(kvals)
+    vc[1, 0, 0], vc[1, 1, 0], vc[0, 0, 0] = codes(vvals)
+    po, plse = oracle.paged_decode_attention_e4m3(q[None], kc, vc, np.array([[1, 0]]), np.array([3]), 2, ks, vs,
+                                                  0.7)
+    ok &= np.allclose(po[0], want, rtol=1e-13, atol=0)
+    po2, _ = oracle.paged_decode_attention_e4m3(q[None], kc, vc, np.array([[1, 0]]), np.array([3]), 2, ks, vs, 0.7,
+                                                pairs=[(0, 1)])
+    ok &= np.allclose(po2[0], want[1], rtol=1e-13, atol=0)
+    return bool(ok)
+
+
 PINS = [pin_worked_example, pin_two_keys_logistic, pin_rows_sum_to_one, pin_identical_keys_mean,
         pin_zero_scale_mean, pin_single_key_exact, pin_lse_scipy, pin_torch_sdpa, pin_gqa_mapping,
         pin_brute_force_recurrences, pin_split_invariance, pin_merge_forms_agree,
-        pin_paged_equals_contiguous]
+        pin_paged_equals_contiguous, pin_e4m3_decoding, pin_e4m3_attention]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -327,6 +369,8 @@ MUTANTS = {
                                lambda L, chunk: [(s, s + chunk) for s in range(0, (L // chunk) * chunk, chunk)]),
     "merge_ignores_lse": ("merge_lse", lambda O_s, lse_s: (np.asarray(O_s).mean(axis=0), float(np.max(lse_s)))),
     "page_slot_swapped": ("gather_pages", None),
+    "e4m3_bias_8": ("E4M3_TABLE", None),
+    "e4m3_scales_swapped": ("decode_attention_e4m3", None),
 }
 
 
@@ -340,10 +384,22 @@ def _bad_gather(cache, table_row, L, page_size):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    if fn is None:
-        fn = _bad_gather
-    monkeypatch.setattr(od, attr, fn)
-    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    if attr == "E4M3_TABLE":
+        import oracle.fp8 as of
+        bad = np.array([of.e4m3_value(c) / 2.0 for c in range(256)])  # exponent bias 8
+        monkeypatch.setattr(of, "E4M3_TABLE", bad)
+    elif attr == "decode_attention_e4m3":
+        import oracle.fp8 as of
+        good = of.dequantize_e4m3
+
+        def swapped(codes, scale):  # K gets v_scale and V gets k_scale
+            return good(codes, {0.25: 3.0, 3.0: 0.25}.get(scale, scale))
+        monkeypatch.setattr(of, "dequantize_e4m3", swapped)
+    else:
+        if fn is None:
+            fn = _bad_gather
+        monkeypatch.setattr(od, attr, fn)
+        monkeypatch.setattr(oracle, attr, fn, raising=False)
     results = {}
     for pin in PINS:
         try:
