@@ -49,15 +49,49 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-    return x;
+// ---------------------------------------------------------------- lane pairs across rows
+// The two values of lanes l and l ^ MASK (MASK = 16: neighbouring rows; 32: the
+// two wave halves), from gfx950's v_permlane16_swap / v_permlane32_swap (VALU
+// lane swaps, no LDS round trip). Both lanes of a pair receive the same two
+// values in the same order (the lower row's or half's first), so any combine
+// written in terms of (lo, hi) gives bit-identical results in both lanes.
+struct LanePair {
+    float lo, hi;
+};
+
+template <int MASK>
+__device__ __forceinline__ LanePair lane_pair(float x) {
+    static_assert(MASK == 16 || MASK == 32, "rows (16) or halves (32)");
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    unsigned r0, r1;  // copied out of the returned vector before any bit_cast
+    if constexpr (MASK == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    }
+    return {__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    return x;
+template <int MASK>
+__device__ __forceinline__ float pair_max(float x) {
+    const LanePair p = lane_pair<MASK>(x);
+    return fmaxf(p.lo, p.hi);
 }
+
+template <int MASK>
+__device__ __forceinline__ float pair_sum(float x) {
+    const LanePair p = lane_pair<MASK>(x);
+    return p.lo + p.hi;
+}
+
+// Max / sum over the whole wave; every lane receives the same value.
+__device__ __forceinline__ float wave_max(float x) { return pair_max<32>(pair_max<16>(row16_max(x))); }
+
+__device__ __forceinline__ float wave_sum(float x) { return pair_sum<32>(pair_sum<16>(row16_sum(x))); }
 
 // ---------------------------------------------------------------- math
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
@@ -287,57 +321,6 @@ struct KvRow<fp8e4m3> {
 // states rescales both to the larger max ("FlashAttention 与推理算子", section
 // "FlashAttention：分块 + online softmax"). An empty state has m = -inf, l = 0.
 __device__ __forceinline__ float finite_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
-
-// ---------------------------------------------------------------- LSE merge
-// One wave merges the n partials of one (sequence, head): split s holds a
-// normalised output O_s (ws row s) and the natural-log lse_s of its scores.
-// With M = max lse_s and w_s = exp(lse_s - M): o = sum w_s O_s / sum w_s
-// ("[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节";
-// equal to the (m, l) merge of "FlashAttention 与推理算子", section "decode 阶段的
-// 并行：Flash-Decoding 与 split-K", since lse_s = m_s + ln l_s). Each lane owns
-// two adjacent output elements. Splits go in batches of kMergeBatch: the
-// batch's partial rows and lse values are all loaded before any of them is
-// used, so a batch costs one round trip to memory; lane i holds split
-// s0 + i's weight and readlane broadcasts it. n == 0 gives 0.
-constexpr int kMergeBatch = 32;
-
-// Partial sums of one wave over splits [s_lo, s_hi) against a given max mu:
-// returns (sum w_s O_s[2 lane], sum w_s O_s[2 lane + 1]) and adds this lane's
-// share of sum w_s to *wpart.
-__device__ __forceinline__ float2 merge_range(const float *ws_o_row, const float *lse_row, int s_lo, int s_hi,
-                                              float mu, int lane, float *wpart) {
-    const float2 *src = reinterpret_cast<const float2 *>(ws_o_row) + lane;
-    float o0 = 0.f, o1 = 0.f;
-    for (int s0 = s_lo; s0 < s_hi; s0 += kMergeBatch) {
-        const int cnt = min(kMergeBatch, s_hi - s0);
-        // Rows past the batch re-read its last row (a valid address) and get
-        // weight 0, so every load is unconditional.
-        float2 x[kMergeBatch];
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) x[u] = src[(size_t)(s0 + min(u, cnt - 1)) * (kHeadDim / 2)];
-        const float w = lane < cnt ? exp2_fast((lse_row[s0 + lane] - mu) * kLog2e) : 0.f;
-        *wpart += w;
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
-            o0 = __builtin_fmaf(wu, x[u].x, o0);
-            o1 = __builtin_fmaf(wu, x[u].y, o1);
-        }
-    }
-    return make_float2(o0, o1);
-}
-
-// Whole merge of one (sequence, head) by a single wave.
-__device__ __forceinline__ float2 merge_partials(const float *ws_o_row, const float *lse_row, int n, int lane) {
-    float mx = -INFINITY;
-    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, lse_row[s]);
-    const float mu = finite_or_zero(wave_max(mx));
-    float wpart = 0.f;
-    const float2 o = merge_range(ws_o_row, lse_row, 0, n, mu, lane, &wpart);
-    const float wsum = wave_sum(wpart);
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    return make_float2(o.x * inv, o.y * inv);
-}
 
 template <typename T>
 struct Pair;

@@ -275,8 +275,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
                 x[sb * 4 + i] = valid ? s[sb][i] * a.scale_log2 : -INFINITY;
                 mt = fmaxf(mt, x[sb * 4 + i]);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = pair_max<32>(pair_max<16>(mt));
         const float m_new = fmaxf(m, mt);
         const float mu = finite_or_zero(m_new);
         const float alpha = exp2_fast(m - mu);
@@ -339,8 +338,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     }
 
     // Head c's running sum over the wave: the four lane groups hold disjoint tokens.
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = pair_sum<32>(pair_sum<16>(lsum));
 
     __syncthreads();  // every wave is done with its V region; reuse it for the merge
     float *s_acc = reinterpret_cast<float *>(s_buf);  // [wave][head][d]

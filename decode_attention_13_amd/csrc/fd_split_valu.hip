@@ -21,8 +21,8 @@
 // online softmax"; the exp2 form with scale*log2(e) folded into the scores as
 // in "[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel 实现细节")
 // and the P.V accumulation in fp32. The 16 per-group states of a workgroup
-// are merged once at the end (DPP-free lane shuffles inside a wave, LDS across
-// waves) and written as a normalised partial plus its natural-log lse, or,
+// are merged once at the end (lane swaps across rows inside a wave, LDS
+// across waves) and written as a normalised partial plus its natural-log lse, or,
 // when one split covers the sequence, as the final output.
 #include "fd_device.h"
 #include "fd_internal.h"
@@ -207,26 +207,28 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     }
 
     // Merge the four 16-lane groups of each wave: lanes c, c^16, c^32, c^48 own
-    // the same head-dim elements.
-#pragma unroll
-    for (int mask = 16; mask <= 32; mask <<= 1) {
+    // the same head-dim elements. Rows pair up first (lane ^ 16), then halves
+    // (lane ^ 32); both lanes of a pair compute the same merged state.
+    auto merge_groups = [&](auto pair) {
 #pragma unroll
         for (int gi = 0; gi < GT; ++gi) {
-            const float mo = __shfl_xor(m[gi], mask, 64);
-            const float lo = __shfl_xor(l[gi], mask, 64);
-            const float M = fmaxf(m[gi], mo);
+            const LanePair pm = pair(m[gi]);
+            const LanePair pl = pair(l[gi]);
+            const float M = fmaxf(pm.lo, pm.hi);
             const float mu = finite_or_zero(M);
-            const float a1 = exp2_fast(m[gi] - mu);
-            const float a2 = exp2_fast(mo - mu);
-            l[gi] = a1 * l[gi] + a2 * lo;
+            const float a_lo = exp2_fast(pm.lo - mu);
+            const float a_hi = exp2_fast(pm.hi - mu);
+            l[gi] = a_lo * pl.lo + a_hi * pl.hi;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xo = __shfl_xor(acc[gi][e], mask, 64);
-                acc[gi][e] = a1 * acc[gi][e] + a2 * xo;
+                const LanePair px = pair(acc[gi][e]);
+                acc[gi][e] = a_lo * px.lo + a_hi * px.hi;
             }
             m[gi] = M;
         }
-    }
+    };
+    merge_groups([](float x) { return lane_pair<16>(x); });
+    merge_groups([](float x) { return lane_pair<32>(x); });
     if (grp == 0) {
 #pragma unroll
         for (int gi = 0; gi < GT; ++gi) {
