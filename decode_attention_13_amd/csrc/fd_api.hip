@@ -118,8 +118,9 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     if (opt && opt->force_chunk > 0) {
         chunk = opt->force_chunk;
     } else if (opt && opt->force_num_splits > 0) {
-        const long long per = ((long long)std::max(max_len, 1) + opt->force_num_splits - 1) / opt->force_num_splits;
-        chunk = (per + FD_CHUNK_QUANTUM - 1) / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
+        // the largest quantum multiple not above max_len / n: about n splits
+        const long long per = (long long)max_len / opt->force_num_splits;
+        chunk = std::max<long long>(FD_CHUNK_QUANTUM, per / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM);
     } else {
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
@@ -128,22 +129,28 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
-    if (page_size > 0) {  // the split's slice of the block table must fit the LDS stage
-        const long long cap = (long long)(fd::kMaxSplitPages - 1) * page_size / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
+    // A split spans up to 2*chunk - 1 tokens (the last one takes the remainder),
+    // i.e. up to (2*chunk - 2) / page_size + 2 pages, and its slice of the block
+    // table must fit the LDS stage of kMaxSplitPages entries.
+    const long long page_cap =
+        page_size > 0 ? ((long long)(fd::kMaxSplitPages - 2) * page_size + 2) / 2 : (long long)1 << 40;
+    if (page_size > 0) {
+        const long long cap = page_cap / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
         if (chunk > cap) {
             if (opt && opt->force_chunk > 0)
-                return fail(FD_ERR_INVALID_ARG, "force_chunk %d spans more than %d pages of %d tokens",
-                            opt->force_chunk, fd::kMaxSplitPages - 1, page_size);
+                return fail(FD_ERR_INVALID_ARG, "force_chunk %d: a split could span more than %d pages of %d tokens",
+                            opt->force_chunk, fd::kMaxSplitPages, page_size);
             chunk = std::max<long long>(cap, FD_CHUNK_QUANTUM);
         }
     }
-    long long splits = std::max(1LL, ((long long)max_len + chunk - 1) / chunk);
+    // max(1, floor(max_len / chunk)) splits: the last one of a sequence takes the remainder.
+    long long splits = std::max(1LL, (long long)max_len / chunk);
     if (splits > kMaxSplits) {
         chunk = ((long long)max_len + kMaxSplits - 1) / kMaxSplits;
         chunk = (chunk + FD_CHUNK_QUANTUM - 1) / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
-        if (page_size > 0 && chunk > (long long)(fd::kMaxSplitPages - 1) * page_size)
+        if (chunk > page_cap)
             return fail(FD_ERR_UNSUPPORTED, "sequence of %d tokens needs more than %d splits", max_len, kMaxSplits);
-        splits = std::max(1LL, ((long long)max_len + chunk - 1) / chunk);
+        splits = std::max(1LL, (long long)max_len / chunk);
     }
 
     std::memset(p, 0, sizeof(*p));

@@ -363,13 +363,24 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
     } else {
         const int L_raw = a.seq_lens[b];
         const int first = t_begin >> a.page_shift;
-        const int last = min((t_begin + a.chunk - 1) >> a.page_shift, a.max_blocks - 1);
+        // a split spans at most 2*chunk - 1 tokens (the last one takes the remainder)
+        const int last = min((t_begin + 2 * a.chunk - 2) >> a.page_shift, a.max_blocks - 1);
         const int32_t *row = a.block_table + (size_t)b * a.max_blocks + first;
         for (int i = threadIdx.x; i <= last - first; i += blockDim.x) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
         __syncthreads();
         *page_first = first;
         return max(0, min(L_raw, a.max_len));
     }
+}
+
+// ---------------------------------------------------------------- split boundaries
+// A sequence of L tokens has max(1, floor(L / chunk)) splits (none if L = 0):
+// split s covers [s*chunk, (s+1)*chunk) except the last, which runs to L and so
+// also takes the remainder (chunk .. 2*chunk - 1 tokens, or all L < 2*chunk).
+__device__ __forceinline__ int splits_of(int L, int chunk) { return L <= 0 ? 0 : max(1, L / chunk); }
+
+__device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
+    return split == n - 1 ? L : (split + 1) * chunk;
 }
 
 // ---------------------------------------------------------------- split epilogue

@@ -12,8 +12,8 @@
 namespace fd {
 
 // Most physical pages one split may touch: the paged split kernel stages the
-// split's block-table slice in LDS. The planner keeps chunk / page_size + 1
-// within this bound.
+// split's block-table slice in LDS. A split spans up to 2*chunk - 1 tokens, so
+// the planner keeps (2*chunk - 2) / page_size + 2 within this bound.
 constexpr int kMaxSplitPages = 1024;
 
 constexpr float kLog2eHost = 1.4426950408889634f;  // log2(e), folded into the scale on the host
@@ -33,7 +33,7 @@ struct SplitArgs {
     int H, Hkv, G;          // G = H / Hkv
     int heads_per_wg;       // query heads of one KV head computed by one workgroup
     int max_len;            // contiguous: S; paged: clamp bound for seq_lens
-    int chunk;              // tokens per split
+    int chunk;              // split stride (a sequence's last split also takes the remainder)
     int num_splits;
     int page_shift;         // log2(page_size)
     int max_blocks;

@@ -63,14 +63,15 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     const int t_begin = split * a.chunk;
     int page_first = 0;
     const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
-    if (t_begin >= L) {  // uniform over the workgroup
+    const int n_b = splits_of(L, a.chunk);
+    if (split >= n_b) {  // uniform over the workgroup
         if (split == 0) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = threadIdx.x; i < GT * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
         return;
     }
-    const int t_end = min(t_begin + a.chunk, L);
+    const int t_end = split_end(split, n_b, L, a.chunk);
 
     const char *kbase = reinterpret_cast<const char *>(a.k);
     const char *vbase = reinterpret_cast<const char *>(a.v);
@@ -243,7 +244,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     __syncthreads();
 
     // Merge the waves, then store the split (or the merged output).
-    const int n_b = (L + a.chunk - 1) / a.chunk;
     finish_split<T>(a, b, h0, GT, split, n_b, [&](int gi, int d, float &lse) {
         float M = s_m[0][gi];
 #pragma unroll

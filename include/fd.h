@@ -12,7 +12,8 @@
  *
  * i.e. S = Q K^T * scale, P = softmax(S), O = P V for one query row ("Flash
  * Attention 与推理算子", section "标准注意力的问题"). The KV sequence is cut
- * into splits of `chunk` tokens; a first kernel computes each split's
+ * into splits of `chunk` tokens, the last split also taking the remainder
+ * (see the workspace layout below); a first kernel computes each split's
  * normalised output and log-sum-exp with an online softmax, a second merges
  * the splits by log-sum-exp ("[CUDA 优化实战] 纯手搓 flash decoding sm120",
  * sections "1. flash decoding" and "2. kernel 实现细节"; "FlashAttention 与
@@ -74,8 +75,9 @@ enum {
 
 /* Optional knobs; pass NULL for all defaults. Zero means "automatic". */
 typedef struct fd_options {
-    int force_num_splits; /* > 0: split the longest sequence into about this many splits */
-    int force_chunk;      /* > 0: tokens per split, a multiple of FD_CHUNK_QUANTUM (wins over force_num_splits) */
+    int force_num_splits; /* > 0: about this many splits of the longest sequence (chunk = the largest
+                             multiple of FD_CHUNK_QUANTUM not above max_len / n, at least the quantum) */
+    int force_chunk;      /* > 0: the split stride, a multiple of FD_CHUNK_QUANTUM (wins over force_num_splits) */
     int force_kernel;     /* FD_KERNEL_* */
     int reserved;         /* must be 0 */
     void *split_begin_event; /* hipEvent_t stamped when the split kernel starts executing, or NULL */
@@ -87,8 +89,8 @@ typedef struct fd_options {
 typedef struct fd_plan {
     int kernel;          /* FD_KERNEL_VALU or FD_KERNEL_MFMA */
     int heads_per_group; /* query heads one workgroup computes (they share one KV head) */
-    int chunk;           /* KV tokens per split */
-    int num_splits;      /* splits of the longest sequence = grid y */
+    int chunk;           /* split stride: every split but a sequence's last holds this many tokens */
+    int num_splits;      /* splits of the longest sequence, max(1, floor(max_len / chunk)) = grid y */
     int grid_x, grid_y, grid_z; /* split kernel grid: (KV-head slices, splits, sequences) */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: o written directly */
@@ -103,9 +105,15 @@ typedef struct fd_plan {
  *   ws_o  [B, H, num_splits, D]  normalised output of each split
  *   ws_lse[B, H, num_splits]     natural-log log-sum-exp of each split's scores,
  *                                at byte offset ws_lse_offset.
- * Split s of sequence b covers tokens [s*chunk, min((s+1)*chunk, L_b)). Only
- * the splits s < ceil(L_b / chunk) of sequences with more than one split are
- * written; a sequence that fits one split is written to o directly. The split
+ * Sequence b has n_b = max(1, floor(L_b / chunk)) splits (none when L_b = 0).
+ * Split s < n_b - 1 covers tokens [s*chunk, (s+1)*chunk); the last split covers
+ * [(n_b - 1)*chunk, L_b), i.e. chunk to 2*chunk - 1 tokens (fewer only when it is
+ * the only split), so no split is a short remainder. Only the splits of
+ * sequences with n_b > 1 are written; a sequence with one split is written to
+ * o directly. The pages cut a sequence into ceil(L_b / chunk) splits with a
+ * short last one; folding the remainder into the last full split gives the
+ * same result up to rounding and spares a workgroup that would read few
+ * tokens for a full workgroup's fixed cost. The split
  * kernel stores partials as "[CUDA 优化实战] 纯手搓 flash decoding sm120",
  * section "2. kernel 实现细节" describes: normalised output plus log-sum-exp.
  */

@@ -156,15 +156,19 @@ def split_bounds(L: int, chunk: int) -> list[tuple[int, int]]:
     return [(s, min(s + chunk, L)) for s in range(0, L, chunk)]
 
 
-def split_partials(q, k, v, scale: float, chunk: int, heads=None):
+def split_partials(q, k, v, scale: float, chunk: int, heads=None, bounds=None):
     """Per-split normalised outputs and natural-log lse ([FA] Flash-Decoding; [FD] §2).
 
     Each split's partial is the definition applied to that split's keys only.
+    The splits are ``split_bounds(S, chunk)`` (the pages' cut), or the given
+    ``bounds``: any list of [start, end) token ranges (the method is exact for
+    every partition of the keys).
     Returns ``(O_s [n_heads, n_splits, D], lse_s [n_heads, n_splits])``.
     """
     H, D = q.shape
     heads = list(range(H)) if heads is None else list(heads)
-    bounds = split_bounds(k.shape[0], chunk)
+    if bounds is None:
+        bounds = split_bounds(k.shape[0], chunk)
     O_s = np.zeros((len(heads), len(bounds), D))
     lse_s = np.full((len(heads), len(bounds)), -np.inf)
     for j, (a, b) in enumerate(bounds):
@@ -173,12 +177,12 @@ def split_partials(q, k, v, scale: float, chunk: int, heads=None):
 
 
 def paged_split_partials(q, k_cache, v_cache, block_table, seq_lens, page_size: int, scale: float,
-                         chunk: int, b: int, h: int):
+                         chunk: int, b: int, h: int, bounds=None):
     """Split partials of one (sequence b, q head h) of a paged batch: ``(O_s [n, D], lse_s [n])``."""
     table, lens = _ints(block_table), _ints(seq_lens)
     kb = gather_pages(k_cache, table[b], lens[b], page_size)
     vb = gather_pages(v_cache, table[b], lens[b], page_size)
-    O_s, lse_s = split_partials(q[b], kb, vb, scale, chunk, heads=[h])
+    O_s, lse_s = split_partials(q[b], kb, vb, scale, chunk, heads=[h], bounds=bounds)
     return O_s[0], lse_s[0]
 
 

@@ -45,7 +45,8 @@ def test_status_strings():
 
 def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
     assert p["chunk"] % 64 == 0 and p["chunk"] >= 64
-    assert p["num_splits"] == max(1, -(-max_len // p["chunk"]))
+    # floor: the last split of a sequence also takes the remainder
+    assert p["num_splits"] == max(1, max_len // p["chunk"])
     assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
     gt = p["heads_per_group"]
     assert (H // Hkv) % gt == 0 and p["grid_x"] == Hkv * (H // Hkv) // gt
@@ -72,13 +73,15 @@ def test_plan_of_each_workload(name):
 
 
 def test_plan_forced_splits_and_chunks():
-    for n in (1, 2, 3, 7, 1000):
+    for n in (1, 2, 3, 7, 64):
         p = fd.decode_plan(32, 32, 4099, "bf16", 256, fd.options(force_num_splits=n))
         _check_plan(p, 4099, 1, 32, 32)
-        assert p["num_splits"] <= n
+        assert p["num_splits"] == n  # 4099 / n rounded down to the quantum gives exactly n here
+    p = fd.decode_plan(32, 32, 4099, "bf16", 256, fd.options(force_num_splits=1000))
+    assert p["chunk"] == 64 and p["num_splits"] == 4099 // 64
     for c in (64, 192, 1024, 8192):
         p = fd.decode_plan(32, 32, 4099, "bf16", 256, fd.options(force_chunk=c))
-        assert p["chunk"] == c and p["num_splits"] == -(-4099 // c)
+        assert p["chunk"] == c and p["num_splits"] == max(1, 4099 // c)
     # more CUs never means fewer splits
     a = fd.decode_plan(32, 32, 131072, "bf16", 64)
     b = fd.decode_plan(32, 32, 131072, "bf16", 256)
@@ -91,7 +94,7 @@ def test_plan_forced_splits_and_chunks():
 def test_plan_paged_chunk_fits_block_table_stage():
     for ps in (1, 2, 16, 64, 256, 1024):
         p = fd.paged_plan(2, 8, 8, "bf16", ps, 1 << 20, 2 << 20, 256)
-        pages = p["chunk"] // ps + 1
+        pages = (2 * p["chunk"] - 2) // ps + 2  # a split spans up to 2*chunk - 1 tokens
         assert pages <= 1024
     with pytest.raises(fd.FdError) as e:
         fd.paged_plan(2, 8, 8, "bf16", 1, 100000, 0, 256, fd.options(force_chunk=2048))

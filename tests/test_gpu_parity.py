@@ -177,6 +177,35 @@ def test_partials_of_long_peaked(device, long_peaked):
         np.testing.assert_allclose(ws_lse[0, h].cpu().numpy(), lse_s[0], rtol=1e-5, atol=5e-4)
 
 
+def kernel_split_bounds(L: int, chunk: int) -> list:
+    """Token ranges of the library's splits (include/fd.h, workspace layout):
+    max(1, floor(L / chunk)) splits, the last one running to L."""
+    n = max(1, L // chunk) if L > 0 else 0
+    return [(s * chunk, L if s == n - 1 else (s + 1) * chunk) for s in range(n)]
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_partials_last_split_takes_the_remainder(kernel, device):
+    """S = 1000 with a 64-token stride: 15 splits, the last one 104 tokens long; the
+    workspace partials against the oracle over the same token ranges."""
+    d = inputs.single_inputs(8, 2, 1000, 128, "bf16", 95, peak_frac=0.01)
+    opt = fd.options(force_chunk=64, kernel=kernel)
+    plan = fd.decode_plan(8, 2, 1000, "bf16", 0, opt)
+    assert plan["num_splits"] == 15 and plan["merge"] == 1
+    ws = fd.new_workspace(plan["workspace_bytes"], device)
+    announce(f"remainder partials {kernel}")
+    o = run_single(d, device, opt=opt, ws=ws)
+    ws_o, ws_lse = fd.workspace_views(ws, plan, 1, 8)
+    bounds = kernel_split_bounds(1000, 64)
+    assert bounds[-1] == (896, 1000)
+    O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], 64, bounds=bounds)
+    for h in range(8):
+        assert_close(ws_o[0, h], O_s[h], "bf16", f"partials head {h}")
+        np.testing.assert_allclose(ws_lse[0, h].cpu().numpy(), lse_s[h], rtol=1e-5, atol=5e-4)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    assert_close(o, ref, "bf16", "merged")
+
+
 def _sample_pairs(B, H, lens, n, seed):
     rng = np.random.default_rng(seed)
     order = np.argsort(lens)

@@ -198,16 +198,19 @@ def pin_brute_force_recurrences() -> bool:
 
 
 def pin_split_invariance() -> bool:
-    """merge(partials(chunk)) == full attention for chunks that do and do not divide S."""
+    """merge(partials) == full attention for chunks that do and do not divide S, and for
+    explicit partitions with unequal ranges (a long last range, a one-token range)."""
     H, Hkv, S, D = 4, 2, 1001, 32
     q = RNG.standard_normal((H, D))
     k = RNG.standard_normal((S, Hkv, D)) * 2
     v = RNG.standard_normal((S, Hkv, D))
     o_full, lse_full = oracle.decode_attention(q, k, v, 0.2)
     ok = True
-    for chunk in (1, 7, 16, 64, 1000, S, 4096):
-        O_s, lse_s = oracle.split_partials(q, k, v, 0.2, chunk)
-        ok &= O_s.shape[1] == -(-S // chunk)
+    cases = [(chunk, None) for chunk in (1, 7, 16, 64, 1000, S, 4096)]
+    cases += [(0, [(0, 64), (64, 128), (128, S)]), (0, [(0, 1), (1, 500), (500, S)])]
+    for chunk, bounds in cases:
+        O_s, lse_s = oracle.split_partials(q, k, v, 0.2, chunk, bounds=bounds)
+        ok &= O_s.shape[1] == (-(-S // chunk) if bounds is None else len(bounds))
         for h in range(H):
             o, lse = oracle.merge_lse(O_s[h], lse_s[h])
             ok &= np.allclose(o, o_full[h], rtol=1e-12, atol=1e-13)
