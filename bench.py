@@ -151,7 +151,8 @@ def inputs_dtype(name: str):
 
 def time_steps(case: Case, steps: int, warmup: int) -> dict:
     """Whole-step wall time over exactly `steps` steps, then the split kernel alone
-    (events on the launch stream around each split kernel) over another `steps`."""
+    (its start and end stamped by the dispatch itself, on the launch stream) over
+    another `steps` steps that follow `warmup` untimed ones."""
     import torch
 
     for i in range(warmup):
@@ -174,6 +175,8 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
                             kernel=base.force_kernel if base else 0,
                             split_begin_event=begins[i], split_end_event=ends[i]) for i in range(steps)]
     torch.cuda.synchronize()
+    for i in range(warmup):  # back to steady state after the synchronisations
+        case.step(i)
     for i in range(steps):
         case.step(i, opts[i])
     torch.cuda.synchronize()
