@@ -194,16 +194,27 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
         }
     };
 
+    // The compute of a tile sits in both arms of the prefetch branch, so the
+    // compiler's wait before it counts only the current tile's loads (a single
+    // copy after the branch would wait for the prefetched tile as well).
     Raw kA[kRows][NL], vA[kRows][NL], kB[kRows][NL], vB[kRows][NL];
     int j = wave;
     if (j < ntiles) load_tile(j, kA, vA);
     while (j < ntiles) {
-        if (j + kWaves < ntiles) load_tile(j + kWaves, kB, vB);
-        compute_tile(j, kA, vA);
+        if (j + kWaves < ntiles) {
+            load_tile(j + kWaves, kB, vB);
+            compute_tile(j, kA, vA);
+        } else {
+            compute_tile(j, kA, vA);
+        }
         j += kWaves;
         if (j >= ntiles) break;
-        if (j + kWaves < ntiles) load_tile(j + kWaves, kA, vA);
-        compute_tile(j, kB, vB);
+        if (j + kWaves < ntiles) {
+            load_tile(j + kWaves, kA, vA);
+            compute_tile(j, kB, vB);
+        } else {
+            compute_tile(j, kB, vB);
+        }
         j += kWaves;
     }
 
