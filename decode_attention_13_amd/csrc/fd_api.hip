@@ -53,13 +53,27 @@ long long pow2_floor(long long x) {
 //    round trip to HBM) and its partial write, short enough to spread short
 //    caches over the chip.
 constexpr int kTargetWgsPerCu = 4;
-constexpr int kTargetWgsPerCuPaged = 16;
+// Paged batches: a workgroup pays a fixed cost (block-table and first KV round
+// trips, the end-of-split merge and partial store) worth about kWgFixedBytes of
+// streaming at its share of the bandwidth, and a ragged batch ends with about
+// half a workgroup of imbalance per resident slot. Balancing the two terms gives
+// a workgroup size of sqrt(2 * bytes per slot * kWgFixedBytes). Measured on the
+// GQA4 and GQA8 batches (bf16/f16 and E4M3 caches): best strides 1024 and 2048.
+constexpr double kWgFixedBytes = 32768.0;
+constexpr int kPagedSlotsPerCu = 2;  // resident split workgroups per CU (two waves per SIMD)
 constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 16384;
 constexpr int kMaxSplits = 4096;
 
 std::mutex g_cu_mutex;
 std::vector<int> g_cu_cache;
+
+// Bytes of one cached K or V element.
+int cache_elem_bytes(fd_dtype d) {
+    if (d == FD_DTYPE_F32) return 4;
+    if (fd::is_fp8_cache(d)) return 1;
+    return 2;
+}
 
 // Heads per workgroup of the vector-ALU kernel: the largest compiled group
 // size dividing G (a workgroup reads its KV rows once for all its heads).
@@ -121,11 +135,17 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         // the largest quantum multiple not above max_len / n: about n splits
         const long long per = (long long)max_len / opt->force_num_splits;
         chunk = std::max<long long>(FD_CHUNK_QUANTUM, per / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM);
+    } else if (page_size > 0) {
+        const double row_bytes = 2.0 * FD_HEAD_DIM * cache_elem_bytes(dtype);  // K + V of one (token, KV head)
+        const double per_slot = (double)std::max(total, 1LL) * Hkv * row_bytes / ((double)num_cus * kPagedSlotsPerCu);
+        const double tokens = std::sqrt(2.0 * per_slot * kWgFixedBytes) / row_bytes;
+        chunk = 1LL << std::max(0L, std::lround(std::log2(std::max(tokens, 1.0))));  // nearest power of two
+        chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     } else {
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
         const long long work = std::max(total, 1LL) * slices;
-        const long long target = (long long)num_cus * (page_size > 0 ? kTargetWgsPerCuPaged : kTargetWgsPerCu);
+        const long long target = (long long)num_cus * kTargetWgsPerCu;
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }

@@ -32,6 +32,8 @@
 // in bf16 and in f16) and the same 16-bit MFMAs run. The per-tensor scales are
 // applied in fp32: k_scale inside the folded softmax scale, v_scale on the
 // normalised output.
+#include <type_traits>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -146,7 +148,7 @@ struct KvFrag<T, fp8e4m3> {
 };
 
 template <typename T, typename KV, int MODE>
-__global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
     using F = KvFrag<T, KV>;
@@ -249,14 +251,18 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
     // of the next two tiles are in flight while this tile is computed.
     uint4 kx[2][KR];
     typename F::VRaw vA[8], vB[8];
-    auto tile = [&](int j, typename F::VRaw (&vcur)[8]) {
+    // REFILL_V / REFILL_K (std::bool_constant) say at compile time whether this
+    // tile refills the V set with tile j + 2*kWaves and K with tile j + kWaves,
+    // so the loads are not under a branch and the compiler's waits count only
+    // the loads a value really depends on.
+    auto tile = [&](int j, typename F::VRaw (&vcur)[8], auto refill_v, auto refill_k) {
         const int t0 = t_begin + j * kTile;
         // V tile -> LDS (row r = token t0 + r, padded rows), then refill the set
         // with the tile after next.
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             *(lds_u32x4 *)(vreg + (4 * i + g) * kRowPad + c * 16) = F::v_lds(vcur[i]);
-        if (j + 2 * kWaves < ntiles) load_v(j + 2 * kWaves, vcur);
+        if constexpr (decltype(refill_v)::value) load_v(j + 2 * kWaves, vcur);
         // S^T tiles: s[sb][i] = score of token t0 + sb*16 + g*4 + i for head c
         f32x4 s[2];
 #pragma unroll
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) s[sb] = M::mma(F::k_operand(kx[sb], kk), qb[kk], s[sb]);
         }
-        if (j + kWaves < ntiles) load_k(j + kWaves, kx);
+        if constexpr (decltype(refill_k)::value) load_k(j + kWaves, kx);
         float x[8];
         float mt = -INFINITY;
 #pragma unroll
@@ -324,19 +330,38 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(SplitArgs a) {
             acc[db] = M::mma(va, pl, acc[db]);
         }
     };
+    using Yes = std::true_type;
+    using No = std::false_type;
     int j = wave;
-    if (j < ntiles) {
+    if (j + 3 * kWaves < ntiles) {
+        // Steady state, two tiles per trip: both refill, so every trip issues the
+        // same loads and the loop carries an exact count of loads in flight.
+        load_k(j, kx);
+        load_v(j, vA);
+        load_v(j + kWaves, vB);
+        do {
+            tile(j, vA, Yes{}, Yes{});
+            tile(j + kWaves, vB, Yes{}, Yes{});
+            j += 2 * kWaves;
+        } while (j + 3 * kWaves < ntiles);
+    } else if (j < ntiles) {
         load_k(j, kx);
         load_v(j, vA);
         if (j + kWaves < ntiles) load_v(j + kWaves, vB);
     }
-    while (j < ntiles) {
-        tile(j, vA);
-        j += kWaves;
-        if (j >= ntiles) break;
-        tile(j, vB);
-        j += kWaves;
-    }
+    // At most three tiles of this wave remain (V sets vA, vB, vA).
+    auto last_tiles = [&](int jj, typename F::VRaw (&vset)[8]) {
+        if (jj + 2 * kWaves < ntiles) {
+            tile(jj, vset, Yes{}, Yes{});
+        } else if (jj + kWaves < ntiles) {
+            tile(jj, vset, No{}, Yes{});
+        } else {
+            tile(jj, vset, No{}, No{});
+        }
+    };
+    if (j < ntiles) last_tiles(j, vA);
+    if (j + kWaves < ntiles) last_tiles(j + kWaves, vB);
+    if (j + 2 * kWaves < ntiles) last_tiles(j + 2 * kWaves, vA);
 
     // Head c's running sum over the wave: the four lane groups hold disjoint tokens.
     lsum = pair_sum<32>(pair_sum<16>(lsum));
