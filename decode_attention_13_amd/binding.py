@@ -38,10 +38,11 @@ class FdPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("heads_per_group", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("num_splits", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("grid_z", ctypes.c_int), ("threads", ctypes.c_int), ("merge", ctypes.c_int),
-                ("reserved", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("ws_lse_offset", ctypes.c_size_t)]
+                ("kv_heads_per_group", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
+                ("ws_lse_offset", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class FdError(RuntimeError):

@@ -53,6 +53,9 @@ long long pow2_floor(long long x) {
 //    round trip to HBM) and its partial write, short enough to spread short
 //    caches over the chip.
 constexpr int kTargetWgsPerCu = 4;
+// With KV heads packed per workgroup (MHA), two workgroups per CU measured best
+// (4k and 128k tokens, bf16 and E4M3 caches): each reads hp rows per token.
+constexpr int kTargetWgsPerCuPacked = 2;
 // Paged batches: a workgroup pays a fixed cost (block-table and first KV round
 // trips, the end-of-split merge and partial store) worth about kWgFixedBytes of
 // streaming at its share of the bandwidth, and a ragged batch ends with about
@@ -126,7 +129,14 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     if (kernel < 0)
         return fail(FD_ERR_UNSUPPORTED, "the matrix-core kernel needs f16/bf16 and H/Hkv <= 16 or a multiple of 16");
     const int gt = kernel == FD_KERNEL_MFMA ? mfma_heads_per_group(G) : valu_heads_per_group(G);
-    const long long slices = (long long)Hkv * (G / gt);
+    // MHA on the vector ALUs: adjacent KV heads share a workgroup so that each load
+    // instruction reads their contiguous rows (512 B; 4 heads for 128-B E4M3 rows).
+    int hp = 1;
+    if (kernel == FD_KERNEL_VALU && G == 1) {
+        hp = fd::is_fp8_cache(dtype) ? 4 : 2;
+        while (hp > 1 && Hkv % hp != 0) hp /= 2;
+    }
+    const long long slices = (long long)(Hkv / hp) * (G / gt);
 
     long long chunk;
     if (opt && opt->force_chunk > 0) {
@@ -136,8 +146,9 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         const long long per = (long long)max_len / opt->force_num_splits;
         chunk = std::max<long long>(FD_CHUNK_QUANTUM, per / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM);
     } else if (page_size > 0) {
-        const double row_bytes = 2.0 * FD_HEAD_DIM * cache_elem_bytes(dtype);  // K + V of one (token, KV head)
-        const double per_slot = (double)std::max(total, 1LL) * Hkv * row_bytes / ((double)num_cus * kPagedSlotsPerCu);
+        const double row_bytes = 2.0 * FD_HEAD_DIM * cache_elem_bytes(dtype) * hp;  // K + V of one token, per workgroup
+        const double per_slot =
+            (double)std::max(total, 1LL) * (Hkv / hp) * row_bytes / ((double)num_cus * kPagedSlotsPerCu);
         const double tokens = std::sqrt(2.0 * per_slot * kWgFixedBytes) / row_bytes;
         chunk = 1LL << std::max(0L, std::lround(std::log2(std::max(tokens, 1.0))));  // nearest power of two
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
@@ -145,7 +156,7 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
         const long long work = std::max(total, 1LL) * slices;
-        const long long target = (long long)num_cus * kTargetWgsPerCu;
+        const long long target = (long long)num_cus * (hp > 1 ? kTargetWgsPerCuPacked : kTargetWgsPerCu);
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
@@ -186,6 +197,7 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     p->grid_z = B;
     p->threads = 256;
     p->merge = splits > 1 ? 1 : 0;
+    p->kv_heads_per_group = hp;
     if (p->merge) {
         const size_t rows = (size_t)B * H * splits;
         const size_t o_bytes = rows * FD_HEAD_DIM * sizeof(float);
@@ -228,7 +240,8 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
     const int mode = !paged ? fd::kContig : ((1 << a.page_shift) >= 16 ? fd::kPagedBlock : fd::kPagedRow);
     hipError_t e = plan.kernel == FD_KERNEL_MFMA
                        ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, shape, a, stream, ev0, ev1)
-                       : fd::launch_split_valu(dtype, plan.heads_per_group, mode, shape, a, stream, ev0, ev1);
+                       : fd::launch_split_valu(dtype, plan.heads_per_group, plan.kv_heads_per_group, mode, shape, a,
+                                               stream, ev0, ev1);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
     if (plan.merge) {
         m.ws_o = a.ws_o;

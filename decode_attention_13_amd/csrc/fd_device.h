@@ -93,6 +93,25 @@ __device__ __forceinline__ float wave_max(float x) { return pair_max<32>(pair_ma
 
 __device__ __forceinline__ float wave_sum(float x) { return pair_sum<32>(pair_sum<16>(row16_sum(x))); }
 
+// Threads of a split-kernel workgroup (both split kernels run 4 waves); a
+// constant rather than blockDim, which would cost a late kernel-argument load.
+constexpr int kSplitThreads = 256;
+
+// ---------------------------------------------------------------- kernel arguments
+// Marks kernel-argument values as used at this point (an empty asm reading them
+// from scalar registers). Called at kernel entry, it makes the compiler fetch
+// them with the first kernel-argument load instead of sinking a second scalar
+// load, a full memory round trip, behind an early-exit branch.
+template <typename T>
+__device__ __forceinline__ void pin_arg(const T &x) {
+    asm volatile("" ::"s"(x));
+}
+
+template <typename... Ts>
+__device__ __forceinline__ void pin_args(const Ts &...xs) {
+    (pin_arg(xs), ...);
+}
+
 // ---------------------------------------------------------------- math
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32
@@ -366,7 +385,8 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
         // a split spans at most 2*chunk - 1 tokens (the last one takes the remainder)
         const int last = min((t_begin + 2 * a.chunk - 2) >> a.page_shift, a.max_blocks - 1);
         const int32_t *row = a.block_table + (size_t)b * a.max_blocks + first;
-        for (int i = threadIdx.x; i <= last - first; i += blockDim.x) s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
+        for (int i = threadIdx.x; i <= last - first; i += kSplitThreads)
+            s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
         __syncthreads();
         *page_first = first;
         return max(0, min(L_raw, a.max_len));
@@ -392,7 +412,7 @@ __device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
 template <typename T, typename ValueFn>
 __device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int split, int n_b, ValueFn value) {
     const bool direct = n_b == 1;
-    for (int i = threadIdx.x; i < nh * kHeadDim; i += blockDim.x) {
+    for (int i = threadIdx.x; i < nh * kHeadDim; i += kSplitThreads) {
         const int hh = i / kHeadDim;
         const int d = i - hh * kHeadDim;
         float lse;

@@ -67,11 +67,12 @@ struct LaunchShape {
     dim3 block;
 };
 
-// Each returns hipSuccess or the launch error. `gt` = heads per workgroup,
+// Each returns hipSuccess or the launch error. `gt` = query heads per KV head in a
+// workgroup, `hp` = adjacent KV heads per workgroup (vector-ALU kernel, MHA),
 // `mode` = AddrMode of fd_device.h (contiguous, paged by 16-token block, paged by row).
 // `start`/`stop` (may be NULL) are timestamped by the dispatch itself at the
 // kernel's start and end (hipExtLaunchKernel), so they time the kernel alone.
-hipError_t launch_split_valu(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, const LaunchShape &shape, const SplitArgs &a,
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &shape, const SplitArgs &a,
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop);

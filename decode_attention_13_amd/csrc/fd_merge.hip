@@ -78,6 +78,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    pin_args(a.ws_o, a.ws_lse, a.out, a.H);
     int L = a.max_len;
     if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
     const int n = min(splits_of(L, a.chunk), a.num_splits);

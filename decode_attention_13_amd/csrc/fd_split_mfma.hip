@@ -41,7 +41,7 @@ namespace fd {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kSplitThreads;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;                // tokens per wave tile
 constexpr int kRowPad = 288;             // LDS bytes per V row: 256 + 32 keeps 8 rows on disjoint banks
@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int g = lane >> 4;   // 16-lane group
     const int c = lane & 15;   // row/column inside the 16x16 tile
     const int split = blockIdx.y;
+    pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
     const int G = a.G;
     const int slices = G / a.heads_per_wg;
     const int kvh = blockIdx.x / slices;

@@ -88,13 +88,15 @@ typedef struct fd_options {
 /* What a call with the same arguments would launch. */
 typedef struct fd_plan {
     int kernel;          /* FD_KERNEL_VALU or FD_KERNEL_MFMA */
-    int heads_per_group; /* query heads one workgroup computes (they share one KV head) */
+    int heads_per_group; /* query heads of one KV head that one workgroup computes (they share its rows) */
     int chunk;           /* split stride: every split but a sequence's last holds this many tokens */
     int num_splits;      /* splits of the longest sequence, max(1, floor(max_len / chunk)) = grid y */
-    int grid_x, grid_y, grid_z; /* split kernel grid: (KV-head slices, splits, sequences) */
+    int grid_x, grid_y, grid_z; /* split kernel grid: (head slices = Hkv / kv_heads_per_group *
+                                   (H / Hkv) / heads_per_group, splits, sequences) */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: o written directly */
-    int reserved;
+    int kv_heads_per_group; /* adjacent KV heads one workgroup reads together (vector-ALU kernel with
+                               H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
     size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
 } fd_plan;

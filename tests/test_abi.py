@@ -48,8 +48,9 @@ def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
     # floor: the last split of a sequence also takes the remainder
     assert p["num_splits"] == max(1, max_len // p["chunk"])
     assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
-    gt = p["heads_per_group"]
-    assert (H // Hkv) % gt == 0 and p["grid_x"] == Hkv * (H // Hkv) // gt
+    gt, hp = p["heads_per_group"], p["kv_heads_per_group"]
+    assert (H // Hkv) % gt == 0 and Hkv % hp == 0 and (hp == 1 or H == Hkv)
+    assert p["grid_x"] == (Hkv // hp) * (H // Hkv) // gt
     if p["merge"]:
         rows = B * H * p["num_splits"]
         assert p["ws_lse_offset"] >= rows * 128 * 4 and p["ws_lse_offset"] % 256 == 0
@@ -140,11 +141,16 @@ def test_decode_rejects_bad_pointers_without_a_device():
 
 
 def test_fp8_cache_plans_and_dtype_routing():
-    # E4M3 caches plan like their query type: same kernel choice and split shape
+    # E4M3 caches plan like their query type (same kernel choice and split shape),
+    # except that MHA packs 4 KV heads (128-B rows) per workgroup instead of 2
     for q_name, code in (("f16", 3), ("bf16", 4)):
         for H, Hkv in ((32, 32), (32, 4), (64, 8), (8, 1)):
             a = fd.decode_plan(H, Hkv, 4096, q_name, 256)
             b = fd.decode_plan(H, Hkv, 4096, code, 256)
+            if H == Hkv:
+                assert (a["kv_heads_per_group"], b["kv_heads_per_group"]) == (2, 4)
+                assert b["num_splits"] * b["chunk"] >= a["num_splits"] * a["chunk"] // 2
+                continue
             assert a == b
         a = fd.paged_plan(64, 32, 8, q_name, 16, 8192, 300000, 256)
         b = fd.paged_plan(64, 32, 8, f"{q_name}_kv_e4m3", 16, 8192, 300000, 256)

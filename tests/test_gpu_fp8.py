@@ -122,6 +122,18 @@ def test_split_and_chunk_invariance(dtype, H, Hkv, kernel, device):
         assert_close(single(d, device, opt=opt), ref, f"H{H}/{Hkv} kernel {plan['kernel']} chunk {plan['chunk']}")
 
 
+@pytest.mark.parametrize("H", [2, 4, 6, 12])
+def test_mha_packed_kv_heads(H, device):
+    """H = Hkv with 128-B E4M3 rows: 4 KV heads per workgroup when Hkv % 4 == 0, else 2."""
+    d = inputs.with_fp8_kv(inputs.single_inputs(H, H, 1500, 128, "bf16", 360 + H))
+    ref = ref_single(d)
+    for opt in (None, fd.options(force_chunk=64)):
+        plan = fd.decode_plan(H, H, 1500, "bf16_kv_e4m3", 0, opt)
+        assert plan["kv_heads_per_group"] == (4 if H % 4 == 0 else 2)
+        announce(f"mha packed H={H} hp={plan['kv_heads_per_group']} chunk {plan['chunk']}")
+        assert_close(single(d, device, opt=opt), ref, f"H={H} chunk {plan['chunk']}")
+
+
 @pytest.mark.parametrize("S", [0, 1, 17, 33, 65, 257, 1000])
 def test_ragged_lengths(S, device):
     d = inputs.with_fp8_kv(inputs.single_inputs(8, 2, S, 128, "bf16", 320 + S))

@@ -275,6 +275,42 @@ def test_head_groups(H, Hkv, kernel, device):
     assert_close(o, ref, "bf16", f"H={H} Hkv={Hkv} {kernel}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("H", [1, 2, 3, 5, 6, 12, 32])
+def test_mha_packed_kv_heads(H, dtype, device):
+    """H = Hkv: the vector-ALU kernel reads 2 adjacent KV heads per workgroup when
+    Hkv is even (1 otherwise); ragged 777 tokens, strides 64 and automatic."""
+    d = inputs.single_inputs(H, H, 777, 128, dtype, 400 + H)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    for opt in (None, fd.options(force_chunk=64), fd.options(force_num_splits=1)):
+        plan = fd.decode_plan(H, H, 777, dtype, 0, opt)
+        assert plan["kv_heads_per_group"] == (2 if H % 2 == 0 else 1)
+        announce(f"mha packed H={H} {dtype} hp={plan['kv_heads_per_group']} chunk {plan['chunk']}")
+        assert_close(run_single(d, device, opt=opt), ref, dtype, f"H={H} chunk {plan['chunk']}")
+
+
+@pytest.mark.parametrize("ps", [1, 16])
+def test_paged_mha_packed_is_bit_exact(ps, device):
+    """Paged MHA (6 heads: packed in pairs): shuffled pages == in-order pages bit for bit,
+    NaN poison unread, and the oracle within tolerance."""
+    lens = [1, 17, 1000, 3000]
+    kA, vA, tA, kB, vB, tB = _pools(lens, 6, ps, "bf16", 410 + ps)
+    q = inputs.normal(np.random.SeedSequence(411), (4, 6, 128), "bf16")
+    L = torch.tensor(lens, dtype=torch.int32)
+    outs = []
+    for kc, vc, t in ((kA, vA, tA), (kB, vB, tB)):
+        announce(f"paged mha packed ps={ps}")
+        o = fd.fd_paged_decode(q.to(device), kc.to(device), vc.to(device), t.to(device), L.to(device), ps,
+                               scale=0.09, max_seq_len=max(lens), total_kv=sum(lens),
+                               opt=fd.options(force_chunk=256))
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.isfinite(outs[0].float()).all()
+    assert torch.equal(outs[0], outs[1])
+    ref, _ = oracle.paged_decode_attention(q, kB, vB, tB, L, ps, 0.09)
+    assert_close(outs[1], ref, "bf16", f"paged mha ps={ps}")
+
+
 # ------------------------------------------------------------------ paged addressing
 
 
