@@ -39,10 +39,10 @@ class FdPlan(ctypes.Structure):
                 ("num_splits", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("grid_z", ctypes.c_int), ("threads", ctypes.c_int), ("merge", ctypes.c_int),
                 ("kv_heads_per_group", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
-                ("ws_lse_offset", ctypes.c_size_t)]
+                ("ws_lse_offset", ctypes.c_size_t), ("work_list", ctypes.c_int), ("reserved2", ctypes.c_int)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_}
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved2"}
 
 
 class FdError(RuntimeError):

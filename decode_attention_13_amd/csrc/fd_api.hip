@@ -44,11 +44,10 @@ long long pow2_floor(long long x) {
     return p;
 }
 
-// Planner constants (measured on MI355X, see the tuning notes of the design).
-//  - Workgroups aimed at per compute unit: a split-kernel workgroup is 4 waves,
-//    each with one or two tiles of K/V in flight, so a few resident workgroups
-//    per CU keep the HBM queues full. A paged batch has ragged lengths, so it
-//    is cut finer: small splits spread long sequences over the whole chip.
+// Planner constants (measured on MI355X).
+//  - Workgroups aimed at per compute unit (contiguous caches): a split-kernel
+//    workgroup is 4 waves, each with one or two tiles of K/V in flight, so a few
+//    resident workgroups per CU keep the HBM queues full.
 //  - Chunk bounds: long enough to amortise a workgroup's start (q load, first
 //    round trip to HBM) and its partial write, short enough to spread short
 //    caches over the chip.
@@ -79,10 +78,11 @@ int cache_elem_bytes(fd_dtype d) {
 }
 
 // Heads per workgroup of the vector-ALU kernel: the largest compiled group
-// size dividing G (a workgroup reads its KV rows once for all its heads).
-int valu_heads_per_group(int G) {
+// size dividing G (a workgroup reads its KV rows once for all its heads). fp32
+// rows stop at 4 heads: 8 heads of fp32 state and rows exceed the registers.
+int valu_heads_per_group(int G, fd_dtype dtype) {
     for (int gt : {8, 4, 2, 1})
-        if (G % gt == 0) return gt;
+        if (G % gt == 0 && !(gt == 8 && dtype == FD_DTYPE_F32)) return gt;
     return 1;
 }
 
@@ -122,13 +122,13 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
 
 // Shared planner. `max_len` is the longest sequence, `total` the sum of the
 // lengths (one sequence for contiguous decode), `page_size` 0 when contiguous.
-fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long long total, int page_size,
-                    int num_cus, const fd_options *opt, fd_plan *p) {
+fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long long total, bool total_known,
+                    int page_size, int num_cus, const fd_options *opt, fd_plan *p) {
     const int G = H / Hkv;
     const int kernel = pick_kernel(dtype, G, opt ? opt->force_kernel : FD_KERNEL_AUTO);
     if (kernel < 0)
         return fail(FD_ERR_UNSUPPORTED, "the matrix-core kernel needs f16/bf16 and H/Hkv <= 16 or a multiple of 16");
-    const int gt = kernel == FD_KERNEL_MFMA ? mfma_heads_per_group(G) : valu_heads_per_group(G);
+    const int gt = kernel == FD_KERNEL_MFMA ? mfma_heads_per_group(G) : valu_heads_per_group(G, dtype);
     // MHA on the vector ALUs: adjacent KV heads share a workgroup so that each load
     // instruction reads their contiguous rows (512 B; 4 heads for 128-B E4M3 rows).
     int hp = 1;
@@ -198,6 +198,19 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     p->threads = 256;
     p->merge = splits > 1 ? 1 : 0;
     p->kv_heads_per_group = hp;
+    // Work list: sequence b has at most 1 + L_b / chunk splits, so a known total
+    // bounds the items by B + total / chunk. When the full grid would be more
+    // than twice that, launch that many workgroups instead. An understated
+    // total_kv leaves items without a workgroup; their outputs become NaN.
+    if (page_size > 0 && total_known && B > 1 && B <= fd::kMaxListSeqs) {
+        const long long items = (long long)B + total / chunk;
+        const long long full = (long long)B * splits;
+        if (full >= 2 * items) {
+            p->work_list = 1;
+            p->grid_y = (int)std::min(items, full);
+            p->grid_z = 1;
+        }
+    }
     if (p->merge) {
         const size_t rows = (size_t)B * H * splits;
         const size_t o_bytes = rows * FD_HEAD_DIM * sizeof(float);
@@ -231,6 +244,9 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
     }
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
+    a.B = B;
+    a.work_list = plan.work_list;
+    a.grid_items = plan.grid_y;
     fd::LaunchShape shape{dim3(plan.grid_x, plan.grid_y, plan.grid_z), dim3(plan.threads)};
 
     hipEvent_t ev0 = opt ? reinterpret_cast<hipEvent_t>(opt->split_begin_event) : nullptr;
@@ -278,7 +294,7 @@ fd_status fd_decode_plan(int H, int Hkv, int S, int D, fd_dtype dtype, int num_c
     if (s != FD_OK) return s;
     if (S < 0) return fail(FD_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
     if ((s = resolve_cus(&num_cus)) != FD_OK) return s;
-    return make_plan(1, H, Hkv, dtype, S, S, 0, num_cus, opt, out);
+    return make_plan(1, H, Hkv, dtype, S, S, true, 0, num_cus, opt, out);
 }
 
 fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_size, int max_seq_len,
@@ -291,7 +307,7 @@ fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_s
     if (max_seq_len < 0) return fail(FD_ERR_INVALID_ARG, "max_seq_len must be >= 0");
     if ((s = resolve_cus(&num_cus)) != FD_OK) return s;
     const long long total = total_kv > 0 ? total_kv : (long long)B * max_seq_len;
-    return make_plan(B, H, Hkv, dtype, max_seq_len, total, page_size, num_cus, opt, out);
+    return make_plan(B, H, Hkv, dtype, max_seq_len, total, total_kv > 0, page_size, num_cus, opt, out);
 }
 
 }  // extern "C"

@@ -403,6 +403,80 @@ __device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
     return split == n - 1 ? L : (split + 1) * chunk;
 }
 
+// ---------------------------------------------------------------- work list
+// Paged launches whose grid would be mostly empty splits (a batch far shorter
+// than its longest sequence) number the splits that hold tokens instead:
+// sequence b contributes max(1, splits_of(L_b)) items (one item writes the zeros
+// of an empty sequence), s_start[b] = items before b, s_start[B] = the total.
+// Every thread of the workgroup must call this (it holds barriers). B <= kMaxListSeqs.
+__device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start, int *s_wave) {
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    int cnt[4];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
+        const int bb = 4 * t + j;
+        int n = 0;
+        if (bb < a.B) n = max(1, splits_of(max(0, min(a.seq_lens[bb], a.max_len)), a.chunk));
+        cnt[j] = n;
+        local += n;
+    }
+    int x = local;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+    int excl = base + x - local;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int bb = 4 * t + j;
+        if (bb < a.B) s_start[bb] = excl;
+        excl += cnt[j];
+    }
+    if (t == kSplitThreads - 1) s_start[a.B] = excl;  // the last thread's end is the total
+    __syncthreads();
+    return s_start[a.B];
+}
+
+// The sequence of work item `item`: the largest b with s_start[b] <= item (every
+// sequence has at least one item, so s_start increases strictly).
+__device__ __forceinline__ int find_sequence(const int *s_start, int B, int item) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_start[mid] <= item) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// When total_kv understated the batch, items past the grid have no workgroup.
+// Their results become NaN instead of silently missing: the output rows of
+// one-split sequences, and the LSE of the missing splits of the others (the
+// merge then yields NaN). Run by one workgroup.
+template <typename T>
+__device__ void poison_unlisted(const SplitArgs &a, const int *s_start, int items) {
+    const float nan = __builtin_nanf("");
+    for (int item = a.grid_items; item < items; ++item) {
+        const int b = find_sequence(s_start, a.B, item);
+        const int n = s_start[b + 1] - s_start[b];
+        const int split = item - s_start[b];
+        if (n == 1) {
+            T *o = reinterpret_cast<T *>(a.out) + (size_t)b * a.H * kHeadDim;
+            for (int i = threadIdx.x; i < a.H * kHeadDim; i += kSplitThreads) o[i] = Elem<T>::store_cast(nan);
+        } else {
+            for (int h = threadIdx.x; h < a.H; h += kSplitThreads)
+                a.ws_lse[((size_t)b * a.H + h) * a.num_splits + split] = nan;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- split epilogue
 // Stores one workgroup's result for query heads h0 .. h0+nh-1 of sequence b,
 // split `split` of n_b. value(hh, d, lse) returns the split's normalised

@@ -40,7 +40,13 @@ struct SplitArgs {
     int num_pages;
     float scale_log2;       // scale * k_scale * log2(e)
     float v_scale;          // dequantisation scale of V (1 unless the cache is FP8)
+    int B;                  // sequences (paged)
+    int work_list;          // 1: grid y numbers the splits that hold tokens (paged; see the split kernels)
+    int grid_items;         // grid y when work_list is set
 };
+
+// Sequences a work-list launch can hold (its per-sequence offsets live in LDS).
+constexpr int kMaxListSeqs = 1024;
 
 // Query/output dtype of a call (FP8-cache codes map to their query type).
 inline fd_dtype query_dtype(fd_dtype d) {

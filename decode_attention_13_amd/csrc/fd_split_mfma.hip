@@ -148,7 +148,7 @@ struct KvFrag<T, fp8e4m3> {
 };
 
 template <typename T, typename KV, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b, const int split) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
     using F = KvFrag<T, KV>;
@@ -158,14 +158,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;   // 16-lane group
     const int c = lane & 15;   // row/column inside the 16x16 tile
-    const int split = blockIdx.y;
-    pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
     const int G = a.G;
     const int slices = G / a.heads_per_wg;
     const int kvh = blockIdx.x / slices;
     const int h0 = kvh * G + (blockIdx.x - kvh * slices) * a.heads_per_wg;
     const int nh = a.heads_per_wg;  // heads of this workgroup (<= 16)
-    const int b = blockIdx.z;
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
     __shared__ __attribute__((aligned(16))) char s_buf[kWaves * kVRegion];
@@ -394,6 +391,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         lse = (Mx + log2_fast(l)) * kLn2;
         return a.v_scale * (o / l);
     });
+}
+
+// One workgroup per (head slice, split, sequence); with a work list (paged
+// batches much shorter than their longest sequence), the splits that hold
+// tokens are numbered sequence by sequence and workgroup y takes items y,
+// y + grid_items, ...: no workgroup is launched only to find its split empty.
+template <typename T, typename KV, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
+    pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
+    int b = blockIdx.z, split = blockIdx.y;
+    if constexpr (MODE != kContig) {
+        if (a.work_list) {
+            __shared__ int s_start[kMaxListSeqs + 1];
+            __shared__ int s_wave[kSplitThreads / 64];
+            const int items = build_work_list(a, s_start, s_wave);
+            const int item = blockIdx.y;
+            if (item == a.grid_items - 1 && blockIdx.x == 0 && items > a.grid_items)
+                poison_unlisted<T>(a, s_start, items);  // total_kv was short: fail loudly
+            if (item >= items) return;
+            b = find_sequence(s_start, a.B, item);
+            split = item - s_start[b];
+        }
+    }
+    split_mfma_item<T, KV, MODE>(a, b, split);
 }
 
 template <typename T, typename KV, int MODE>

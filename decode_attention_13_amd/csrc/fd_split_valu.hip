@@ -43,7 +43,7 @@ constexpr int kWaves = kThreads / 64;
 // (measured with a plain read kernel on the 32-head layout: 12.7 against 10.8 us
 // for 64 MB).
 template <typename T, typename KV, int GT, int HP, int MODE>
-__global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
+__device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b, const int split) {
     static_assert(HP == 1 || GT == 1, "packed KV heads are for MHA");
     constexpr bool PAGED = MODE != kContig;
     using E = Elem<T>;
@@ -61,8 +61,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     const int c = lane & 15;
     const int hs = grp % HP;  // this group's KV head within the workgroup
     const int ts = grp / HP;  // this group's token within a load instruction
-    const int split = blockIdx.y;
-    pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
     int kvh, h0;
     if constexpr (HP > 1) {  // G = 1: query head = KV head
         kvh = blockIdx.x * HP;
@@ -72,7 +70,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
         kvh = blockIdx.x / slices;
         h0 = kvh * a.G + (blockIdx.x - kvh * slices) * GT;
     }
-    const int b = blockIdx.z;
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
     __shared__ float s_m[kWaves][NH];
@@ -295,6 +292,30 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
         lse = (M + log2_fast(lsum)) * kLn2;
         return a.v_scale * (o / lsum);
     });
+}
+
+// One workgroup per (head slice, split, sequence); with a work list (paged
+// batches much shorter than their longest sequence), the splits that hold
+// tokens are numbered sequence by sequence and workgroup y takes items y,
+// y + grid_items, ...: no workgroup is launched only to find its split empty.
+template <typename T, typename KV, int GT, int HP, int MODE>
+__global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
+    pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
+    int b = blockIdx.z, split = blockIdx.y;
+    if constexpr (MODE != kContig) {
+        if (a.work_list) {
+            __shared__ int s_start[kMaxListSeqs + 1];
+            __shared__ int s_wave[kSplitThreads / 64];
+            const int items = build_work_list(a, s_start, s_wave);
+            const int item = blockIdx.y;
+            if (item == a.grid_items - 1 && blockIdx.x == 0 && items > a.grid_items)
+                poison_unlisted<T>(a, s_start, items);  // total_kv was short: fail loudly
+            if (item >= items) return;
+            b = find_sequence(s_start, a.B, item);
+            split = item - s_start[b];
+        }
+    }
+    split_valu_item<T, KV, GT, HP, MODE>(a, b, split);
 }
 
 template <typename T, typename KV, int GT, int HP, int MODE>

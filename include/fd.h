@@ -92,13 +92,18 @@ typedef struct fd_plan {
     int chunk;           /* split stride: every split but a sequence's last holds this many tokens */
     int num_splits;      /* splits of the longest sequence, max(1, floor(max_len / chunk)) = grid y */
     int grid_x, grid_y, grid_z; /* split kernel grid: (head slices = Hkv / kv_heads_per_group *
-                                   (H / Hkv) / heads_per_group, splits, sequences) */
+                                   (H / Hkv) / heads_per_group, splits, sequences); see work_list */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: o written directly */
     int kv_heads_per_group; /* adjacent KV heads one workgroup reads together (vector-ALU kernel with
                                H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
     size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
+    int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens, sequence by
+                               sequence, grid_z = 1, and workgroup y takes items y, y + grid_y, ...;
+                               chosen when the (splits x sequences) grid would be mostly empty splits
+                               and total_kv is known */
+    int reserved2;
 } fd_plan;
 
 /*
@@ -172,8 +177,12 @@ fd_status fd_decode(const void *q, const void *k, const void *v, void *o,
  *   o            [B, H, D], fully overwritten
  *   max_seq_len  host-side upper bound of every L_b (sizes the grid; no
  *                device-to-host read of seq_lens ever happens)
- *   total_kv     host-side sum of L_b if known (> 0), else <= 0; used only to
- *                size the splits
+ *   total_kv     host-side sum of L_b (each clamped to max_seq_len and to the
+ *                table's reach) if known (> 0), else <= 0. It sizes the splits
+ *                and, for a batch far shorter than its longest sequence, the
+ *                work-list grid (fd_plan.work_list); a value below the true sum
+ *                may leave splits unlaunched, whose outputs are then NaN. A
+ *                larger value only costs idle workgroups.
  *   Other arguments as in fd_decode.
  */
 fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache,

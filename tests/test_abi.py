@@ -47,7 +47,10 @@ def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
     assert p["chunk"] % 64 == 0 and p["chunk"] >= 64
     # floor: the last split of a sequence also takes the remainder
     assert p["num_splits"] == max(1, max_len // p["chunk"])
-    assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
+    if p["work_list"]:  # splits that hold tokens, numbered; at most the full grid
+        assert p["grid_z"] == 1 and 1 <= p["grid_y"] <= B * p["num_splits"]
+    else:
+        assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
     gt, hp = p["heads_per_group"], p["kv_heads_per_group"]
     assert (H // Hkv) % gt == 0 and Hkv % hp == 0 and (hp == 1 or H == Hkv)
     assert p["grid_x"] == (Hkv // hp) * (H // Hkv) // gt
@@ -90,6 +93,22 @@ def test_plan_forced_splits_and_chunks():
     # S = 0 still has one (empty) split that writes zeros
     z = fd.decode_plan(8, 8, 0, "f32", 256)
     assert z["num_splits"] == 1 and z["merge"] == 0
+
+
+def test_plan_work_list_choice():
+    # GQA8 batch (lengths 256..64k, log-uniform): the full grid would be mostly empty
+    # splits, so a known total switches to the numbered work list
+    w = WORKLOADS["paged_gqa8_f16_b128_s256-64k"]
+    L = w.seq_lens()
+    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+    assert p["work_list"] == 1 and p["grid_z"] == 1
+    assert p["grid_y"] == w.B + int(L.sum()) // p["chunk"]
+    assert p["grid_y"] >= sum(max(1, int(x) // p["chunk"]) for x in L)  # every split has a workgroup
+    # unknown total, contiguous decode, one sequence, uniform lengths: the full grid
+    assert fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256)["work_list"] == 0
+    assert fd.decode_plan(32, 32, 131072, "bf16", 256)["work_list"] == 0
+    assert fd.paged_plan(1, 32, 8, "bf16", 16, 65536, 65536, 256)["work_list"] == 0
+    assert fd.paged_plan(64, 32, 8, "bf16", 16, 8192, 64 * 8192, 256)["work_list"] == 0
 
 
 def test_plan_paged_chunk_fits_block_table_stage():

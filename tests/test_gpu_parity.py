@@ -438,6 +438,67 @@ def test_paged_many_sequences_ragged_splits(device):
         assert_close(got, ref, "bf16", f"chunk={c}")
 
 
+def _ragged_batch(B, seed, lo=1, hi=6000):
+    rng = np.random.default_rng(seed)
+    lens = np.exp(rng.uniform(np.log(lo), np.log(hi), B)).astype(int).tolist()
+    lens[3] = 0  # an empty sequence
+    return lens, inputs.paged_inputs(B, 32, 8, 128, "bf16", 16, lens, seed)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+def test_work_list_matches_grid(kernel, device):
+    """A batch far shorter than its longest sequence: with total_kv the splits that
+    hold tokens are numbered (work list), without it the full (split, sequence) grid
+    runs. Same splits, same arithmetic: bit-identical outputs, and the oracle agrees."""
+    lens, d = _ragged_batch(48, 420)
+    opt = fd.options(force_chunk=256, kernel=kernel)
+    total = sum(lens)
+    p_list = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), total, 0, opt)
+    p_grid = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), 0, 0, opt)
+    assert p_list["work_list"] == 1 and p_grid["work_list"] == 0
+    assert p_list["grid_y"] == 48 + total // 256
+    outs = []
+    for tk in (total, 0):
+        announce(f"work list {kernel} total_kv={tk}")
+        g = to_dev(d, device)
+        outs.append(fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                                       scale=d["scale"], max_seq_len=max(lens), total_kv=tk, opt=opt).cpu())
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.all(outs[0][3] == 0)
+    pairs = _sample_pairs(48, 32, np.array(lens), 6, 421)
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"], pairs=pairs)
+    assert_close(torch.stack([outs[0][b, h] for b, h in pairs]), ref, "bf16", f"work list {kernel}")
+
+
+def test_work_list_short_total_is_nan(device):
+    """total_kv below the true sum: the splits past the shortened work list have no
+    workgroup, and exactly the sequences that own one come out NaN; every other
+    sequence is bit-identical to the full-grid result."""
+    lens, d = _ragged_batch(48, 430)
+    opt = fd.options(force_chunk=256)
+    short = sum(lens) // 3
+    plan = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), short, 0, opt)
+    assert plan["work_list"] == 1
+    counts = [max(1, L // 256) for L in lens]
+    start = np.concatenate([[0], np.cumsum(counts)])
+    missing = [b for b in range(48) if start[b + 1] > plan["grid_y"]]
+    assert missing and len(missing) < 48
+    g = to_dev(d, device)
+    outs = []
+    for tk in (short, 0):
+        announce(f"work list short total_kv={tk}")
+        outs.append(fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                                       scale=d["scale"], max_seq_len=max(lens), total_kv=tk, opt=opt).cpu())
+        torch.cuda.synchronize()
+    for b in range(48):
+        if b in missing:
+            assert torch.isnan(outs[0][b].float()).all(), b
+        else:
+            assert torch.equal(outs[0][b], outs[1][b]), b
+
+
 def test_workspace_too_small_is_rejected(device):
     d = to_dev(inputs.single_inputs(8, 8, 4096, 128, "bf16", 95), device)
     plan = fd.decode_plan(8, 8, 4096, "bf16", 0, fd.options(force_num_splits=4))
