@@ -15,6 +15,7 @@ Contents
                algorithms.
 ``fp8``     -- values of an FP8 E4M3 KV cache with per-tensor scales, and the
                plain definition over them (contiguous and paged).
+``prefill`` -- many-query attention over a prompt with an optional causal mask.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (the pages' worked example, closed forms, a library routine,
@@ -36,6 +37,7 @@ from .decode import (  # noqa: F401
     merge_m_l,
 )
 from . import loops  # noqa: F401
+from .prefill import causal_mask, prefill_attention  # noqa: F401
 from .fp8 import (  # noqa: F401
     dequantize_e4m3,
     e4m3_value,

@@ -325,10 +325,50 @@ def pin_e4m3_attention() -> bool:
     return bool(ok)
 
 
+def pin_prefill_torch_sdpa() -> bool:
+    """Prefill against torch's CPU scaled_dot_product_attention in float64 (is_causal and
+    not), with its own GQA grouping, at N not a multiple of any tile."""
+    ok = True
+    for B, N, H, Hkv, D, causal in ((2, 37, 4, 2, 16, True), (1, 50, 3, 3, 8, False), (1, 1, 2, 1, 4, True)):
+        q = RNG.standard_normal((B, N, H, D))
+        k = RNG.standard_normal((B, N, Hkv, D))
+        v = RNG.standard_normal((B, N, Hkv, D))
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.3, is_causal=causal,
+                                                               enable_gqa=True)
+        o, _ = oracle.prefill_attention(q, k, v, 0.3, causal)
+        ok &= np.allclose(o, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+    return bool(ok)
+
+
+def pin_prefill_rows_are_decodes() -> bool:
+    """Causal row i is the decode of query i over keys 0..i (its lse too); row 0 returns
+    v_0 exactly; identical keys give the running mean of V; non-causal rows see all keys."""
+    B, N, H, Hkv, D = 1, 23, 4, 2, 8
+    q = RNG.standard_normal((B, N, H, D))
+    k = RNG.standard_normal((B, N, Hkv, D))
+    v = RNG.standard_normal((B, N, Hkv, D))
+    o, lse = oracle.prefill_attention(q, k, v, 0.7, True)
+    ok = True
+    for i in (0, 1, 7, 22):
+        od, ld = oracle.decode_attention(q[0, i], k[0, :i + 1], v[0, :i + 1], 0.7)
+        ok &= np.allclose(o[0, i], od, rtol=1e-12, atol=1e-13) and np.allclose(lse[0, i], ld, rtol=1e-12)
+    ok &= np.array_equal(o[0, 0], np.repeat(v[0, 0], 2, axis=0))
+    on, _ = oracle.prefill_attention(q, k, v, 0.7, False)
+    od, _ = oracle.decode_attention(q[0, 5], k[0], v[0], 0.7)
+    ok &= np.allclose(on[0, 5], od, rtol=1e-12, atol=1e-13)
+    kk = np.repeat(k[:, :1], N, axis=1)
+    oi, _ = oracle.prefill_attention(q, kk, v, 0.7, True)
+    means = np.cumsum(v[0], axis=0) / np.arange(1, N + 1)[:, None, None]
+    ok &= np.allclose(oi[0], np.repeat(means, 2, axis=1), rtol=1e-12, atol=1e-13)
+    return bool(ok)
+
+
 PINS = [pin_worked_example, pin_two_keys_logistic, pin_rows_sum_to_one, pin_identical_keys_mean,
         pin_zero_scale_mean, pin_single_key_exact, pin_lse_scipy, pin_torch_sdpa, pin_gqa_mapping,
         pin_brute_force_recurrences, pin_split_invariance, pin_merge_forms_agree,
-        pin_paged_equals_contiguous, pin_e4m3_decoding, pin_e4m3_attention]
+        pin_paged_equals_contiguous, pin_e4m3_decoding, pin_e4m3_attention, pin_prefill_torch_sdpa,
+        pin_prefill_rows_are_decodes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -374,6 +414,8 @@ MUTANTS = {
     "page_slot_swapped": ("gather_pages", None),
     "e4m3_bias_8": ("E4M3_TABLE", None),
     "e4m3_scales_swapped": ("decode_attention_e4m3", None),
+    "causal_off_by_one": ("causal_mask", lambda n_q, n_k: np.arange(n_k)[None, :] < np.arange(n_q)[:, None]),
+    "causal_transposed": ("causal_mask", lambda n_q, n_k: np.arange(n_k)[None, :] >= np.arange(n_q)[:, None]),
 }
 
 
@@ -398,6 +440,9 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         def swapped(codes, scale):  # K gets v_scale and V gets k_scale
             return good(codes, {0.25: 3.0, 3.0: 0.25}.get(scale, scale))
         monkeypatch.setattr(of, "dequantize_e4m3", swapped)
+    elif attr == "causal_mask":
+        import oracle.prefill as opf
+        monkeypatch.setattr(opf, "causal_mask", fn)
     else:
         if fn is None:
             fn = _bad_gather
