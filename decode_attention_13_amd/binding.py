@@ -82,6 +82,9 @@ SIGNATURES = {
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                              ctypes.POINTER(FdOptions), ctypes.c_void_p]),
+    "fd_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                  ctypes.c_int, ctypes.POINTER(FdOptions), ctypes.c_void_p]),
     "fd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fd_last_error": (ctypes.c_char_p, []),
 }
@@ -309,6 +312,29 @@ def fd_paged_decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                        seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), float(k_scale),
                                        float(v_scale), B, H, Hkv, D, num_pages, max_blocks, max_seq_len,
                                        int(total_kv), dt, wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
+    return o
+
+
+def fd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+               scale: float | None = None, causal: bool = True, opt: FdOptions | None = None,
+               stream=None) -> torch.Tensor:
+    """Prefill attention: q [B, N, H, D], k/v [B, N, Hkv, D] (f16/bf16) -> o [B, N, H, D];
+    causal: query i sees keys 0..i."""
+    B, N, H, D = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != N or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("k and v must both be [B, N, Hkv, D] with q's B, N and D")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, q.dtype)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib().fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, N, H, k.shape[2], D,
+                            _dtype_code(q.dtype), float(scale), 1 if causal else 0, _opt_ptr(opt),
+                            _stream_handle(stream)))
     return o
 
 

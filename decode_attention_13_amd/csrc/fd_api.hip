@@ -439,6 +439,38 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
                       D, num_pages, max_blocks, max_seq_len, total_kv, dtype, ws, ws_bytes, opt, stream);
 }
 
+fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B, int N, int H, int Hkv, int D,
+                     fd_dtype dtype, float scale, int causal, const fd_options *opt, void *stream) {
+    fd_status s = check_common(B, H, Hkv, D, dtype, opt);
+    if (s != FD_OK) return s;
+    if (dtype != FD_DTYPE_F16 && dtype != FD_DTYPE_BF16)
+        return fail(FD_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
+    if (N < 0) return fail(FD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+    if (B > 65535 || H > 65535) return fail(FD_ERR_UNSUPPORTED, "B and H must be <= 65535");
+    if (N == 0) return FD_OK;
+    if (!q || !k || !v || !o) return fail(FD_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(FD_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    fd::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.N = N;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.G = H / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.q_tiles = (N + 63) / 64;
+    a.scale_log2 = scale * fd::kLog2eHost;
+    hipEvent_t ev0 = opt ? reinterpret_cast<hipEvent_t>(opt->split_begin_event) : nullptr;
+    hipEvent_t ev1 = opt ? reinterpret_cast<hipEvent_t>(opt->split_end_event) : nullptr;
+    const hipError_t e = fd::launch_prefill(dtype, a, reinterpret_cast<hipStream_t>(stream), ev0, ev1);
+    if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "prefill kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
 const char *fd_status_string(fd_status s) {
     switch (s) {
         case FD_OK: return "FD_OK";

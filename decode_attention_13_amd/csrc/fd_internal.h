@@ -91,4 +91,15 @@ inline hipError_t launch_timed(const void *fn, const LaunchShape &s, void **args
 }
 hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, hipStream_t stream);
 
+// Prefill: q, o [B, N, H, D]; k, v [B, N, Hkv, D].
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    int B, N, H, Hkv, G;    // G = H / Hkv
+    int causal;             // 1: query i sees keys 0 .. i
+    int q_tiles;            // ceil(N / 64)
+    float scale_log2;       // scale * log2(e)
+};
+hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace fd

@@ -1,0 +1,253 @@
+// fd_prefill.hip -- prefill attention (many queries, optional causal mask) on
+// the matrix cores (gfx950, wave64, v_mfma_f32_16x16x32_{bf16,f16}).
+//
+// The blocked algorithm of "FlashAttention 与推理算子", section
+// "FlashAttention：分块 + online softmax": a block of queries walks the key
+// blocks, keeps a running max and sum per query row and rescales its output
+// accumulator; with the causal mask (same section) key blocks past the query
+// block's last row are never visited and the diagonal block is masked element
+// by element. The FlashAttention-2 layout the page describes (each Q block its
+// own workgroup, waves split by query rows) is kept.
+//
+// Workgroup: 64 queries of one head (4 waves x 16), key tiles of 32 tokens
+// staged in LDS and shared by the 4 waves (double buffered: the next tile's
+// global loads are in flight while the current one is computed).
+// Per wave and tile, the matrix-core work is that of the decode kernel with
+// query rows in place of query heads:
+//   S^T[key, q] = K[key, :] . Q[q, :]       two 16x16x32 MFMA chains of 4
+//   online softmax per query (column), log2 domain, fp32
+//   O^T[d, q] += V^T[d, key] . P^T[key, q]  eight 16x16x32 MFMAs (bf16: P split
+//       into two 16-bit parts, two MFMAs each, which keeps P.V near fp32)
+// P^T needs no lane movement (key slot (l/16)*8 + j holds key
+// (j/4)*16 + (l/16)*4 + j%4, the keys of that lane's S accumulators); V^T comes
+// from the LDS tile with ds_read_b64_tr_b16.
+#include <type_traits>
+
+#include "fd_device.h"
+#include "fd_internal.h"
+
+namespace fd {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQTile = 64;     // queries per workgroup
+constexpr int kKTile = 32;     // keys per LDS tile
+constexpr int kKPad = 272;     // LDS bytes per K row (256 + 16)
+constexpr int kVPad = 288;     // LDS bytes per V row (256 + 32, as for the transposed reads)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+    static constexpr bool kSplitP = true;  // bf16 keeps 8 bits of P: use hi + lo
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+    __device__ static uint32_t pack2(float x, float y) {
+        return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
+    }
+    __device__ static float lo_of(uint32_t w) { return bf16_lo(w); }
+    __device__ static float hi_of(uint32_t w) { return bf16_hi(w); }
+};
+
+template <>
+struct Mma<_Float16> {
+    static constexpr bool kSplitP = false;  // f16 keeps 11 bits of P in [0, 1]
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+    __device__ static uint32_t pack2(float x, float y) {
+        return __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
+    }
+    __device__ static float lo_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
+    __device__ static float hi_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+    using M = Mma<T>;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    pin_args(a.q, a.k, a.v, a.o, a.scale_log2);
+    // Query tiles in reverse order: with the causal mask the last tiles hold the
+    // most keys, so they start first.
+    const int qt = a.q_tiles - 1 - (int)blockIdx.x;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int kvh = h / a.G;
+    const int N = a.N;
+    const int q0 = qt * kQTile + wave * 16;  // this wave's first query
+    const int kv_end = a.causal ? min(N, (qt + 1) * kQTile) : N;
+    const int ntiles = (kv_end + kKTile - 1) / kKTile;
+
+    __shared__ __attribute__((aligned(16))) char sK[2][kKTile * kKPad];
+    __shared__ __attribute__((aligned(16))) char sV[2][kKTile * kVPad];
+
+    // Q fragment (B operand of S): query q0 + c, head-dim slots kk*32 + g*8 .. +8.
+    uint4 qb[4];
+    {
+        const int qr = min(q0 + c, N - 1);
+        const T *qrow = reinterpret_cast<const T *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qb[kk] = load16(qrow + kk * 32 + g * 8);
+    }
+
+    // Tile staging: thread t moves 16-byte pieces t and t + 256 of the K and V
+    // tiles (piece p: row p / 16, bytes (p % 16) * 16); rows past N re-read row N - 1.
+    const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
+    const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
+    const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
+    uint4 kst[2], vst[2];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = threadIdx.x + i * kThreads;
+            const int key = min(j * kKTile + (p >> 4), N - 1);
+            const size_t off = (size_t)key * tok_bytes + (p & 15) * 16;
+            kst[i] = load16(kg + off);
+            vst[i] = load16(vg + off);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = threadIdx.x + i * kThreads;
+            *(lds_u32x4 *)(uintptr_t)(sK[buf] + (p >> 4) * kKPad + (p & 15) * 16) =
+                u32x4{kst[i].x, kst[i].y, kst[i].z, kst[i].w};
+            *(lds_u32x4 *)(uintptr_t)(sV[buf] + (p >> 4) * kVPad + (p & 15) * 16) =
+                u32x4{vst[i].x, vst[i].y, vst[i].z, vst[i].w};
+        }
+    };
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;  // running max of query q0 + c (same in the 4 lane groups)
+    float lsum = 0.f;     // this lane's share of the running sum
+    const int q_me = q0 + c;
+
+    auto compute = [&](int j, int buf) {
+        const int key0 = j * kKTile;
+        if (a.causal && key0 > q0 + 15) return;  // every key of the tile is after this wave's queries
+        lds_char *kt = (lds_char *)(uintptr_t)sK[buf];
+        lds_char *vt = (lds_char *)(uintptr_t)sV[buf];
+        f32x4 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x4 kr = *(lds_u32x4 *)(kt + (sb * 16 + c) * kKPad + kk * 64 + g * 16);
+                s[sb] = M::mma(make_uint4(kr.x, kr.y, kr.z, kr.w), qb[kk], s[sb]);
+            }
+        }
+        float x[8];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + sb * 16 + g * 4 + i;
+                const bool valid = key < N && (!a.causal || key <= q_me);
+                x[sb * 4 + i] = valid ? s[sb][i] * a.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, x[sb * 4 + i]);
+            }
+        mt = pair_max<32>(pair_max<16>(mt));
+        const float m_new = fmaxf(m, mt);
+        const float mu = finite_or_zero(m_new);
+        const float alpha = exp2_fast(m - mu);
+        m = m_new;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = exp2_fast(x[e] - mu);
+            ps += p[e];
+        }
+        lsum = lsum * alpha + ps;
+        uint4 ph, pl;
+        {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                hw[e2] = M::pack2(p[2 * e2], p[2 * e2 + 1]);
+                if constexpr (M::kSplitP) lw[e2] = M::pack2(p[2 * e2] - M::lo_of(hw[e2]), p[2 * e2 + 1] - M::hi_of(hw[e2]));
+            }
+            ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if constexpr (M::kSplitP) pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+        }
+        const int e = c >> 2, bq = c & 3;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int col_bytes = (db * 16 + bq * 4) * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(vt + (g * 4 + e) * kVPad + col_bytes));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(vt + (16 + g * 4 + e) * kVPad + col_bytes));
+            const u32x2v lo2 = __builtin_bit_cast(u32x2v, lo);
+            const u32x2v hi2 = __builtin_bit_cast(u32x2v, hi);
+            const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+            acc[db] = M::mma(va, ph, acc[db]);
+            if constexpr (M::kSplitP) acc[db] = M::mma(va, pl, acc[db]);
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const bool more = j + 1 < ntiles;
+        if (more) load_tile(j + 1);
+        compute(j, j & 1);
+        if (more) store_tile((j + 1) & 1);
+        __syncthreads();
+    }
+
+    lsum = pair_sum<32>(pair_sum<16>(lsum));
+    if (q_me < N) {
+        const float inv = 1.f / lsum;
+        T *orow = reinterpret_cast<T *>(a.o) + (((size_t)b * N + q_me) * a.H + h) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            typedef typename Pair<T>::type P2;
+            P2 *dst = reinterpret_cast<P2 *>(orow + db * 16 + g * 4);
+            dst[0] = Pair<T>::make(acc[db][0] * inv, acc[db][1] * inv);
+            dst[1] = Pair<T>::make(acc[db][2] * inv, acc[db][3] * inv);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    LaunchShape s{dim3(a.q_tiles, a.H, a.B), dim3(kThreads)};
+    PrefillArgs arg = a;
+    void *args[] = {&arg};
+    switch (dtype) {
+        case FD_DTYPE_F16: return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<_Float16>), s, args, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16>), s, args, st, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fd

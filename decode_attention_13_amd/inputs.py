@@ -266,6 +266,52 @@ WORKLOADS = {
 }
 
 
+# --------------------------------------------------------------------------- prefill
+
+
+def prefill_inputs(B: int, N: int, H: int, Hkv: int, D: int, dtype: str, seed) -> dict:
+    """q [B, N, H, D], k/v [B, N, Hkv, D] ~ N(0,1) rounded to dtype; scale 1/sqrt(D)."""
+    ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+    return {"q": normal(_child(ss, 0), (B, N, H, D), dtype), "k": normal(_child(ss, 1), (B, N, Hkv, D), dtype),
+            "v": normal(_child(ss, 2), (B, N, Hkv, D), dtype), "scale": default_scale(D)}
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    index: int
+    B: int
+    N: int
+    H: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool
+
+    kind = "prefill"
+
+    def make(self) -> dict:
+        return prefill_inputs(self.B, self.N, self.H, self.Hkv, self.D, self.dtype,
+                              np.random.SeedSequence(1000 + self.index))
+
+    def flops(self) -> int:
+        """Useful flops: 4 * D per (query, visible key) pair and head."""
+        pairs = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return 4 * self.D * pairs * self.B * self.H
+
+
+# The prompt pass of the same model shapes: 32 heads of 128, a 4k prompt, causal;
+# and the GQA-4 shape over two 2k prompts.
+PREFILL_WORKLOADS = {
+    w.name: w for w in [
+        PrefillWorkload("prefill_bf16_h32_n4096_causal", 6, B=1, N=4096, H=32, Hkv=32, D=128, dtype="bf16",
+                        causal=True),
+        PrefillWorkload("prefill_f16_b2_h32_kv8_n2048_causal", 7, B=2, N=2048, H=32, Hkv=8, D=128, dtype="f16",
+                        causal=True),
+    ]
+}
+
+
 def sweep_workload(S: int) -> SingleWorkload:
     """The pages' benchmark shape (32 heads, head_dim 128, bf16) at KV length S."""
     return SingleWorkload(f"decode_bf16_h32_s{S}", 100 + S % 1000003, H=32, Hkv=32, S=S, D=128, dtype="bf16")

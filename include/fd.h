@@ -219,6 +219,26 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
                                 void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
 
 /* Static name of a status code. */
+/*
+ * Prefill attention: many queries over a prompt, optionally causal
+ * ("FlashAttention 与推理算子", sections "标准注意力的问题" and
+ * "FlashAttention：分块 + online softmax", its paragraph on the causal mask of
+ * decoder self-attention). For every sequence b, position i < N and head h:
+ *
+ *     o[b,i,h,:] = sum_j softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) * v[b,j,g,:]
+ *
+ * over keys j < N, or j <= i when causal != 0; g = h / (H / Hkv).
+ *   q, o   [B, N, H, D] row-major; o fully overwritten
+ *   k, v   [B, N, Hkv, D] row-major (per sequence the decode cache layout)
+ *   dtype  FD_DTYPE_F16 or FD_DTYPE_BF16 (matrix cores); D = 128
+ *   N      >= 0 (N = 0 launches nothing); B, H <= 65535
+ *   opt    may be NULL; only split_begin_event / split_end_event are used, and
+ *          they time the prefill kernel
+ * No workspace. Asynchronous on `stream`; errors as for fd_decode.
+ */
+fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B, int N, int H, int Hkv, int D,
+                     fd_dtype dtype, float scale, int causal, const fd_options *opt, void *stream);
+
 const char *fd_status_string(fd_status s);
 
 /* Message of the last failing call on this thread ("" if none). */
