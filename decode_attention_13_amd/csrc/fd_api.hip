@@ -6,6 +6,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cfloat>
+#include <climits>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -446,7 +448,10 @@ fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B
     if (dtype != FD_DTYPE_F16 && dtype != FD_DTYPE_BF16)
         return fail(FD_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
     if (N < 0) return fail(FD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+    if (N > (1 << 30)) return fail(FD_ERR_UNSUPPORTED, "N must be <= 2^30 (got %d)", N);
     if (B > 65535 || H > 65535) return fail(FD_ERR_UNSUPPORTED, "B and H must be <= 65535");
+    if ((long long)B * H * ((N + 63) / 64) > INT_MAX)
+        return fail(FD_ERR_UNSUPPORTED, "B * H * ceil(N / 64) must fit in 31 bits");
     if (N == 0) return FD_OK;
     if (!q || !k || !v || !o) return fail(FD_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -462,8 +467,11 @@ fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B
     a.Hkv = Hkv;
     a.G = H / Hkv;
     a.causal = causal ? 1 : 0;
-    a.q_tiles = (N + 63) / 64;
     a.scale_log2 = scale * fd::kLog2eHost;
+    // The kernel needs a nonzero factor (a masked score must stay -inf after
+    // scaling); with the least normal float every unmasked score still scales to
+    // exactly 0 in exp2, as with a zero scale.
+    if (a.scale_log2 == 0.f) a.scale_log2 = FLT_MIN;
     hipEvent_t ev0 = opt ? reinterpret_cast<hipEvent_t>(opt->split_begin_event) : nullptr;
     hipEvent_t ev1 = opt ? reinterpret_cast<hipEvent_t>(opt->split_end_event) : nullptr;
     const hipError_t e = fd::launch_prefill(dtype, a, reinterpret_cast<hipStream_t>(stream), ev0, ev1);

@@ -97,7 +97,7 @@ struct PrefillArgs {
     void *o;
     int B, N, H, Hkv, G;    // G = H / Hkv
     int causal;             // 1: query i sees keys 0 .. i
-    int q_tiles;            // ceil(N / 64)
+    int q_tiles;            // query tiles (set by the launcher)
     float scale_log2;       // scale * log2(e)
 };
 hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);

@@ -9,7 +9,7 @@
 // by element. The FlashAttention-2 layout the page describes (each Q block its
 // own workgroup, waves split by query rows) is kept.
 //
-// Workgroup: 64 queries of one head (4 waves x 16), key tiles of 32 tokens
+// Workgroup: 64 * QB queries of one head (4 waves x 16 QB), key tiles of 32 tokens
 // staged in LDS and shared by the 4 waves (double buffered: the next tile's
 // global loads are in flight while the current one is computed).
 // Per wave and tile, the matrix-core work is that of the decode kernel with
@@ -31,10 +31,11 @@ namespace fd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQTile = 64;     // queries per workgroup
 constexpr int kKTile = 32;     // keys per LDS tile
 constexpr int kKPad = 272;     // LDS bytes per K row (256 + 16)
 constexpr int kVPad = 288;     // LDS bytes per V row (256 + 32, as for the transposed reads)
+constexpr int kXcds = 8;       // XCDs of the MI355X, each with its own L2
+constexpr float kLazyLog2 = 8.f;  // the running max trails the true one by at most this (log2 units)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -65,7 +66,7 @@ struct Mma<__bf16> {
 
 template <>
 struct Mma<_Float16> {
-    static constexpr bool kSplitP = false;  // f16 keeps 11 bits of P in [0, 1]
+    static constexpr bool kSplitP = false;  // f16 keeps 11 bits of P (P < 2^8: no overflow)
     __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                       0, 0, 0);
@@ -77,35 +78,65 @@ struct Mma<_Float16> {
     __device__ static float hi_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
 };
 
-template <typename T>
+// QB: blocks of 16 queries per wave. Every K and V fragment read from LDS
+// feeds QB MFMA column blocks, so LDS traffic per flop falls as 1 / QB.
+template <typename T, int QB>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     using M = Mma<T>;
+    constexpr int kQTile = 4 * 16 * QB;  // queries per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int c = lane & 15;
     pin_args(a.q, a.k, a.v, a.o, a.scale_log2);
-    // Query tiles in reverse order: with the causal mask the last tiles hold the
-    // most keys, so they start first.
-    const int qt = a.q_tiles - 1 - (int)blockIdx.x;
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // The 1-D grid is dealt round robin over the 8 XCDs (workgroup i runs on XCD
+    // i % 8). Renumber so that XCD x runs the x-th eighth of the (sequence, head,
+    // query tile) items in order: the query tiles of one head share an XCD and
+    // its L2, where the K/V tiles they all walk stay resident. Within a head the
+    // query tiles go in reverse: with the causal mask the last ones hold the most
+    // keys, so they start first.
+    const int total = a.q_tiles * a.H * a.B;
+    const int per_xcd = total / kXcds;
+    const int lin = blockIdx.x;
+    const int slot = lin / kXcds;
+    const int item = slot < per_xcd ? (lin % kXcds) * per_xcd + slot : kXcds * per_xcd + lin % kXcds;
+    const int qt = a.q_tiles - 1 - item % a.q_tiles;
+    const int h = (item / a.q_tiles) % a.H;
+    const int b = item / (a.q_tiles * a.H);
     const int kvh = h / a.G;
     const int N = a.N;
-    const int q0 = qt * kQTile + wave * 16;  // this wave's first query
+    const int q0 = qt * kQTile + wave * 16 * QB;  // this wave's first query
+    const int q_last = q0 + 16 * QB - 1;
     const int kv_end = a.causal ? min(N, (qt + 1) * kQTile) : N;
     const int ntiles = (kv_end + kKTile - 1) / kKTile;
 
     __shared__ __attribute__((aligned(16))) char sK[2][kKTile * kKPad];
     __shared__ __attribute__((aligned(16))) char sV[2][kKTile * kVPad];
 
-    // Q fragment (B operand of S): query q0 + c, head-dim slots kk*32 + g*8 .. +8.
-    uint4 qb[4];
-    {
-        const int qr = min(q0 + c, N - 1);
+    // Q fragments (B operand of S): query q0 + 16*qb + c, head-dim slots kk*32 + g*8 .. +8.
+    uint4 qf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qr = min(q0 + 16 * qb + c, N - 1);
         const T *qrow = reinterpret_cast<const T *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qb[kk] = load16(qrow + kk * 32 + g * 8);
+        for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = load16(qrow + kk * 32 + g * 8);
+    }
+    // A negative scale is moved into Q (a sign flip is exact), so the running
+    // max can be taken over the raw scores and scaled afterwards.
+    // sl > 0 (a zero scale arrives as the least normal float), so -inf * sl
+    // stays -inf and a masked score gives exp2 = 0.
+    const float sl = fabsf(a.scale_log2);
+    if (a.scale_log2 < 0.f) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                qf[qb][kk].x ^= 0x80008000u;
+                qf[qb][kk].y ^= 0x80008000u;
+                qf[qb][kk].z ^= 0x80008000u;
+                qf[qb][kk].w ^= 0x80008000u;
+            }
     }
 
     // Tile staging: thread t moves 16-byte pieces t and t + 256 of the K and V
@@ -135,66 +166,90 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    f32x4 acc[8];
+    f32x4 acc[QB][8];
+    float m[QB], lsum[QB];  // running max (same in the 4 lane groups) and this lane's share of the sum
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;  // running max of query q0 + c (same in the 4 lane groups)
-    float lsum = 0.f;     // this lane's share of the running sum
-    const int q_me = q0 + c;
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    auto compute = [&](int j, int buf) {
+    // Online softmax with a lazy running max: m moves only when a tile's max
+    // exceeds it by more than kLazyLog2 (P then stays below 2^kLazyLog2), so the
+    // accumulators are rescaled a few times per row instead of on most tiles.
+    // Any subtracted constant gives the same softmax; the final division uses the
+    // sum taken with the same constants.
+    auto compute = [&](int j, int buf, bool masked) {
         const int key0 = j * kKTile;
-        if (a.causal && key0 > q0 + 15) return;  // every key of the tile is after this wave's queries
         lds_char *kt = (lds_char *)(uintptr_t)sK[buf];
         lds_char *vt = (lds_char *)(uintptr_t)sV[buf];
-        f32x4 s[2];
+        f32x4 s[QB][2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const u32x4 kr = *(lds_u32x4 *)(kt + (sb * 16 + c) * kKPad + kk * 64 + g * 16);
-                s[sb] = M::mma(make_uint4(kr.x, kr.y, kr.z, kr.w), qb[kk], s[sb]);
+                const uint4 ka = make_uint4(kr.x, kr.y, kr.z, kr.w);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[qb][sb] = M::mma(ka, qf[qb][kk], s[qb][sb]);
             }
         }
-        float x[8];
-        float mt = -INFINITY;
+        uint4 ph[QB], pl[QB];
+        float alpha[QB];
+        bool rescale = false;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int qb = 0; qb < QB; ++qb) {
+            float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = key0 + sb * 16 + g * 4 + i;
-                const bool valid = key < N && (!a.causal || key <= q_me);
-                x[sb * 4 + i] = valid ? s[sb][i] * a.scale_log2 : -INFINITY;
-                mt = fmaxf(mt, x[sb * 4 + i]);
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[sb * 4 + i] = s[qb][sb][i];
+            if (masked) {  // wave-uniform; masked scores become -inf, so their P is exactly 0
+                const int q_me = q0 + 16 * qb + c;
+                const int room = (a.causal ? min(q_me, N - 1) : N - 1) - key0 - g * 4;  // key offset limit
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (sb * 16 + i > room) x[sb * 4 + i] = -INFINITY;
             }
-        mt = pair_max<32>(pair_max<16>(mt));
-        const float m_new = fmaxf(m, mt);
-        const float mu = finite_or_zero(m_new);
-        const float alpha = exp2_fast(m - mu);
-        m = m_new;
-        float p[8];
-        float ps = 0.f;
+            // Raw-score max (the scale is >= 0: its sign was moved into Q).
+            float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            mt = pair_max<32>(pair_max<16>(mt));
+            const float mt_s = mt > -INFINITY ? mt * sl : -INFINITY;
+            const float m_old = m[qb];
+            const float m_new = mt_s > m_old + kLazyLog2 ? mt_s : m_old;
+            alpha[qb] = exp2_fast(m_old - m_new);
+            rescale |= m_new != m_old && m_old > -INFINITY;
+            m[qb] = m_new;
+            const float mu = finite_or_zero(m_new);
+            float p[8];
+            float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = exp2_fast(x[e] - mu);
-            ps += p[e];
-        }
-        lsum = lsum * alpha + ps;
-        uint4 ph, pl;
-        {
+            for (int e = 0; e < 8; ++e) {
+                p[e] = exp2_fast(__builtin_fmaf(x[e], sl, -mu));
+                ps += p[e];
+            }
+            lsum[qb] = m_old > -INFINITY ? __builtin_fmaf(lsum[qb], alpha[qb], ps) : ps;
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 hw[e2] = M::pack2(p[2 * e2], p[2 * e2 + 1]);
-                if constexpr (M::kSplitP) lw[e2] = M::pack2(p[2 * e2] - M::lo_of(hw[e2]), p[2 * e2 + 1] - M::hi_of(hw[e2]));
+                if constexpr (M::kSplitP)
+                    lw[e2] = M::pack2(p[2 * e2] - M::lo_of(hw[e2]), p[2 * e2 + 1] - M::hi_of(hw[e2]));
             }
-            ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            if constexpr (M::kSplitP) pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            ph[qb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if constexpr (M::kSplitP) pl[qb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
         }
         const int e = c >> 2, bq = c & 3;
 #pragma unroll
@@ -207,8 +262,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             const u32x2v lo2 = __builtin_bit_cast(u32x2v, lo);
             const u32x2v hi2 = __builtin_bit_cast(u32x2v, hi);
             const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
-            acc[db] = M::mma(va, ph, acc[db]);
-            if constexpr (M::kSplitP) acc[db] = M::mma(va, pl, acc[db]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                acc[qb][db] = M::mma(va, ph[qb], acc[qb][db]);
+                if constexpr (M::kSplitP) acc[qb][db] = M::mma(va, pl[qb], acc[qb][db]);
+            }
         }
     };
 
@@ -218,34 +276,50 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < ntiles; ++j) {
         const bool more = j + 1 < ntiles;
         if (more) load_tile(j + 1);
-        compute(j, j & 1);
+        const int key0 = j * kKTile;
+        // Wave-uniform: tiles wholly after this wave's queries are skipped;
+        // only tiles that reach the diagonal or the end of the keys are masked.
+        if (!(a.causal && key0 > q_last)) {
+            compute(j, j & 1, key0 + kKTile > N || (a.causal && key0 + kKTile - 1 > q0));
+        }
         if (more) store_tile((j + 1) & 1);
         __syncthreads();
     }
 
-    lsum = pair_sum<32>(pair_sum<16>(lsum));
-    if (q_me < N) {
-        const float inv = 1.f / lsum;
-        T *orow = reinterpret_cast<T *>(a.o) + (((size_t)b * N + q_me) * a.H + h) * kHeadDim;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            typedef typename Pair<T>::type P2;
-            P2 *dst = reinterpret_cast<P2 *>(orow + db * 16 + g * 4);
-            dst[0] = Pair<T>::make(acc[db][0] * inv, acc[db][1] * inv);
-            dst[1] = Pair<T>::make(acc[db][2] * inv, acc[db][3] * inv);
+    for (int qb = 0; qb < QB; ++qb) {
+        const float ls = pair_sum<32>(pair_sum<16>(lsum[qb]));
+        const int q_me = q0 + 16 * qb + c;
+        if (q_me < N) {
+            const float inv = 1.f / ls;
+            T *orow = reinterpret_cast<T *>(a.o) + (((size_t)b * N + q_me) * a.H + h) * kHeadDim;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                typedef typename Pair<T>::type P2;
+                P2 *dst = reinterpret_cast<P2 *>(orow + db * 16 + g * 4);
+                dst[0] = Pair<T>::make(acc[qb][db][0] * inv, acc[qb][db][1] * inv);
+                dst[1] = Pair<T>::make(acc[qb][db][2] * inv, acc[qb][db][3] * inv);
+            }
         }
     }
 }
 
 }  // namespace
 
+constexpr int kQueryBlocks = 1;  // 16-query blocks per wave (2 costs occupancy and measured slower)
+
 hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    LaunchShape s{dim3(a.q_tiles, a.H, a.B), dim3(kThreads)};
     PrefillArgs arg = a;
+    arg.q_tiles = (a.N + 64 * kQueryBlocks - 1) / (64 * kQueryBlocks);
+    LaunchShape s{dim3(arg.q_tiles * a.H * a.B), dim3(kThreads)};
     void *args[] = {&arg};
     switch (dtype) {
-        case FD_DTYPE_F16: return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<_Float16>), s, args, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16>), s, args, st, e0, e1);
+        case FD_DTYPE_F16:
+            return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<_Float16, kQueryBlocks>), s, args, st,
+                                e0, e1);
+        case FD_DTYPE_BF16:
+            return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16, kQueryBlocks>), s, args, st,
+                                e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

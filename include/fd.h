@@ -231,7 +231,9 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
  *   q, o   [B, N, H, D] row-major; o fully overwritten
  *   k, v   [B, N, Hkv, D] row-major (per sequence the decode cache layout)
  *   dtype  FD_DTYPE_F16 or FD_DTYPE_BF16 (matrix cores); D = 128
- *   N      >= 0 (N = 0 launches nothing); B, H <= 65535
+ *   N      0 .. 2^30 (N = 0 launches nothing); B, H <= 65535 and
+ *          B * H * ceil(N / 64) < 2^31 (else FD_ERR_UNSUPPORTED)
+ *   scale  any finite value (a negative one flips the sign of every score)
  *   opt    may be NULL; only split_begin_event / split_end_event are used, and
  *          they time the prefill kernel
  * No workspace. Asynchronous on `stream`; errors as for fd_decode.

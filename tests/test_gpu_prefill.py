@@ -97,3 +97,40 @@ def test_workload_gqa(device):
     heads = [3, 12, 30]
     ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], True, heads=heads)
     assert_close(o[:, :, heads], ref, w.name)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.5, 3.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_scales(scale, causal, device):
+    """A negative scale (its sign goes into Q on the device), a zero scale (every
+    visible key weighs the same), and large scales whose scores spread over many
+    powers of two, so the running max moves by more than the lazy threshold."""
+    d = inputs.prefill_inputs(1, 300, 4, 2, 128, "bf16", 530)
+    announce(f"scale={scale} causal={causal}")
+    o = fd.fd_prefill(d["q"].to(device), d["k"].to(device), d["v"].to(device), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], scale, causal)
+    assert_close(o.cpu(), ref, f"scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rising_scores_rescale_every_tile(dtype, device):
+    """Keys built so that every query's best score grows by about 12 (log2 units)
+    from one 32-key tile to the next: the running max moves on every tile and the
+    accumulators are rescaled each time."""
+    N, D = 256, 128
+    g = torch.Generator().manual_seed(540)
+    q = torch.randn(1, N, 2, D, generator=g) * 0.1
+    q[..., 0] = 1.0
+    k = torch.randn(1, N, 1, D, generator=g) * 0.1
+    k[..., 0] = (torch.arange(N) // 32).to(torch.float32)[None, :, None] * 8.0 / (1.4427 * 0.75)
+    v = torch.randn(1, N, 1, D, generator=g)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    q, k, v = q.to(tdt), k.to(tdt), v.to(tdt)
+    scale = 1.1
+    announce(f"rising scores {dtype}")
+    for causal in (True, False):
+        o = fd.fd_prefill(q.to(device), k.to(device), v.to(device), scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        ref, _ = oracle.prefill_attention(q, k, v, scale, causal)
+        assert_close(o.cpu(), ref, f"rising {dtype} causal={causal}")
