@@ -27,6 +27,13 @@ HIPCC_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Per-file additions. Prefill: keep the MFMA accumulators in ordinary VGPRs
+# (the online-softmax rescale multiplies them on the VALU, which cannot read
+# AGPRs; in AGPRs every tile would copy them out and back).
+EXTRA_FLAGS = {
+    "fd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -57,7 +64,7 @@ def build(verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

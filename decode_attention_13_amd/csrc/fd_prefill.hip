@@ -47,6 +47,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
+__device__ __forceinline__ float max2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+
 template <typename T>
 struct Mma;
 
@@ -85,24 +87,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     using M = Mma<T>;
     constexpr int kQTile = 4 * 16 * QB;  // queries per workgroup
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: wave-level branches stay scalar
     const int g = lane >> 4;
     const int c = lane & 15;
     pin_args(a.q, a.k, a.v, a.o, a.scale_log2);
     // The 1-D grid is dealt round robin over the 8 XCDs (workgroup i runs on XCD
-    // i % 8). Renumber so that XCD x runs the x-th eighth of the (sequence, head,
-    // query tile) items in order: the query tiles of one head share an XCD and
-    // its L2, where the K/V tiles they all walk stay resident. Within a head the
-    // query tiles go in reverse: with the causal mask the last ones hold the most
-    // keys, so they start first.
-    const int total = a.q_tiles * a.H * a.B;
-    const int per_xcd = total / kXcds;
+    // i % 8, as its (i / 8)-th). When the (sequence, head) units divide evenly,
+    // each XCD takes its own eighth of them, so the query tiles of a head share
+    // one L2 where the K/V tiles they all walk stay resident; within an XCD the
+    // tiles go longest first (with the causal mask the last query tiles hold the
+    // most keys), which balances the XCD's workgroup slots. Otherwise the whole
+    // grid goes longest first.
+    const int units = a.H * a.B;
     const int lin = blockIdx.x;
-    const int slot = lin / kXcds;
-    const int item = slot < per_xcd ? (lin % kXcds) * per_xcd + slot : kXcds * per_xcd + lin % kXcds;
-    const int qt = a.q_tiles - 1 - item % a.q_tiles;
-    const int h = (item / a.q_tiles) % a.H;
-    const int b = item / (a.q_tiles * a.H);
+    int unit, qt_rev;
+    if (units % kXcds == 0) {
+        const int per = units / kXcds;
+        const int t = lin / kXcds;
+        unit = (lin % kXcds) * per + t % per;
+        qt_rev = t / per;
+    } else {
+        unit = lin % units;
+        qt_rev = lin / units;
+    }
+    const int qt = a.q_tiles - 1 - qt_rev;
+    const int h = unit % a.H;
+    const int b = unit / a.H;
     const int kvh = h / a.G;
     const int N = a.N;
     const int q0 = qt * kQTile + wave * 16 * QB;  // this wave's first query
@@ -139,30 +149,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             }
     }
 
-    // Tile staging: thread t moves 16-byte pieces t and t + 256 of the K and V
-    // tiles (piece p: row p / 16, bytes (p % 16) * 16); rows past N re-read row N - 1.
+    // Tile staging: thread t moves 16-byte pieces t and t + 256 of a K or V tile
+    // (piece p: row p / 16, bytes (p % 16) * 16); rows past N re-read row N - 1.
     const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
     const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
     const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
-    uint4 kst[2], vst[2];
-    auto load_tile = [&](int j) {
+    auto fetch = [&](const char *src, int j, uint4 (&st)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int p = threadIdx.x + i * kThreads;
             const int key = min(j * kKTile + (p >> 4), N - 1);
-            const size_t off = (size_t)key * tok_bytes + (p & 15) * 16;
-            kst[i] = load16(kg + off);
-            vst[i] = load16(vg + off);
+            st[i] = load16(src + (size_t)key * tok_bytes + (p & 15) * 16);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto put = [&](char *dst, int pad, const uint4 (&st)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int p = threadIdx.x + i * kThreads;
-            *(lds_u32x4 *)(uintptr_t)(sK[buf] + (p >> 4) * kKPad + (p & 15) * 16) =
-                u32x4{kst[i].x, kst[i].y, kst[i].z, kst[i].w};
-            *(lds_u32x4 *)(uintptr_t)(sV[buf] + (p >> 4) * kVPad + (p & 15) * 16) =
-                u32x4{vst[i].x, vst[i].y, vst[i].z, vst[i].w};
+            *(lds_u32x4 *)(uintptr_t)(dst + (p >> 4) * pad + (p & 15) * 16) = u32x4{st[i].x, st[i].y, st[i].z, st[i].w};
         }
     };
 
@@ -176,81 +180,98 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         for (int db = 0; db < 8; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Online softmax with a lazy running max: m moves only when a tile's max
-    // exceeds it by more than kLazyLog2 (P then stays below 2^kLazyLog2), so the
-    // accumulators are rescaled a few times per row instead of on most tiles.
-    // Any subtracted constant gives the same softmax; the final division uses the
-    // sum taken with the same constants.
-    auto compute = [&](int j, int buf, bool masked) {
-        const int key0 = j * kKTile;
-        lds_char *kt = (lds_char *)(uintptr_t)sK[buf];
-        lds_char *vt = (lds_char *)(uintptr_t)sV[buf];
-        f32x4 s[QB][2];
+    struct Scores {
+        f32x4 v[QB][2];
+    };
+    // S^T of one tile from the K buffer.
+    auto scores = [&](int kbuf) {
+        lds_char *kt = (lds_char *)(uintptr_t)sK[kbuf];
+        Scores r;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qb = 0; qb < QB; ++qb) r.v[qb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const u32x4 kr = *(lds_u32x4 *)(kt + (sb * 16 + c) * kKPad + kk * 64 + g * 16);
                 const uint4 ka = make_uint4(kr.x, kr.y, kr.z, kr.w);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb][sb] = M::mma(ka, qf[qb][kk], s[qb][sb]);
+                for (int qb = 0; qb < QB; ++qb) r.v[qb][sb] = M::mma(ka, qf[qb][kk], r.v[qb][sb]);
             }
         }
-        uint4 ph[QB], pl[QB];
-        float alpha[QB];
+        return r;
+    };
+
+    // Online softmax with a lazy running max: m moves only when a tile's max
+    // exceeds it by more than kLazyLog2 (P then stays below 2^kLazyLog2), so the
+    // accumulators are rescaled a few times per row instead of on most tiles.
+    // Any subtracted constant gives the same softmax; the final division uses the
+    // sum taken with the same constants.
+    //
+    // Step 1 (tile_max): mask the tile's scores, update m; returns whether the
+    // accumulators need rescaling (alpha holds the factors).
+    float alpha[QB], mu[QB];
+    auto tile_max = [&](int j, Scores &sc, bool masked) {
         bool rescale = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float x[8];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[sb * 4 + i] = s[qb][sb][i];
             if (masked) {  // wave-uniform; masked scores become -inf, so their P is exactly 0
                 const int q_me = q0 + 16 * qb + c;
-                const int room = (a.causal ? min(q_me, N - 1) : N - 1) - key0 - g * 4;  // key offset limit
+                const int room = (a.causal ? min(q_me, N - 1) : N - 1) - j * kKTile - g * 4;  // key offset limit
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (sb * 16 + i > room) x[sb * 4 + i] = -INFINITY;
+                        if (sb * 16 + i > room) sc.v[qb][sb][i] = -INFINITY;
             }
-            // Raw-score max (the scale is >= 0: its sign was moved into Q).
-            float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mt = pair_max<32>(pair_max<16>(mt));
-            const float mt_s = mt > -INFINITY ? mt * sl : -INFINITY;
+            const f32x4 s0 = sc.v[qb][0], s1 = sc.v[qb][1];
+            // Raw-score max (the scale is > 0: its sign was moved into Q); med3
+            // with +inf is a max that needs no NaN canonicalisation of its inputs.
+            float mt = max2(max2(max2(s0[0], s0[1]), max2(s0[2], s0[3])), max2(max2(s1[0], s1[1]), max2(s1[2], s1[3])));
+            LanePair pr = lane_pair<16>(mt);
+            mt = max2(pr.lo, pr.hi);
+            pr = lane_pair<32>(mt);
+            mt = max2(pr.lo, pr.hi);
+            const float mt_s = mt * sl;  // -inf stays -inf
             const float m_old = m[qb];
             const float m_new = mt_s > m_old + kLazyLog2 ? mt_s : m_old;
-            alpha[qb] = exp2_fast(m_old - m_new);
+            mu[qb] = finite_or_zero(m_new);
+            alpha[qb] = exp2_fast(m_old - mu[qb]);  // 0 while m_old is -inf
             rescale |= m_new != m_old && m_old > -INFINITY;
             m[qb] = m_new;
-            const float mu = finite_or_zero(m_new);
-            float p[8];
+        }
+        return __builtin_amdgcn_ballot_w64(rescale) != 0;
+    };
+
+    // Step 2 (tile_pv): P = exp2(s * sl - mu) and O^T += V^T . P^T from the V
+    // buffer; while the VALU forms P the matrix cores take the scores of the next
+    // tile (the scores MFMAs do not wait for P).
+    auto tile_pv = [&](const Scores &sc, int vbuf, Scores &next, int kbuf_next) {
+        next = scores(kbuf_next);
+        uint4 ph[QB], pl[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float pe[8];
             float ps = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = exp2_fast(__builtin_fmaf(x[e], sl, -mu));
-                ps += p[e];
-            }
-            lsum[qb] = m_old > -INFINITY ? __builtin_fmaf(lsum[qb], alpha[qb], ps) : ps;
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pe[sb * 4 + i] = exp2_fast(__builtin_fmaf(sc.v[qb][sb][i], sl, -mu[qb]));
+                    ps += pe[sb * 4 + i];
+                }
+            lsum[qb] = __builtin_fmaf(lsum[qb], alpha[qb], ps);
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                hw[e2] = M::pack2(p[2 * e2], p[2 * e2 + 1]);
+                hw[e2] = M::pack2(pe[2 * e2], pe[2 * e2 + 1]);
                 if constexpr (M::kSplitP)
-                    lw[e2] = M::pack2(p[2 * e2] - M::lo_of(hw[e2]), p[2 * e2 + 1] - M::hi_of(hw[e2]));
+                    lw[e2] = M::pack2(pe[2 * e2] - M::lo_of(hw[e2]), pe[2 * e2 + 1] - M::hi_of(hw[e2]));
             }
             ph[qb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             if constexpr (M::kSplitP) pl[qb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
-        if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
-        }
+        lds_char *vt = (lds_char *)(uintptr_t)sV[vbuf];
         const int e = c >> 2, bq = c & 3;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
@@ -270,19 +291,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    load_tile(0);
-    store_tile(0);
+    // Software pipeline: the K ring runs one tile ahead of the V ring, so the
+    // scores of tile j + 1 are formed while tile j's P is. Iteration j fetches
+    // K(j + 2) and V(j + 1) from global memory and stores them, after its own
+    // LDS reads, into the buffers that iteration j - 1 finished reading.
+    // Tiles this wave computes: with the causal mask those after its last query
+    // are skipped (the workgroup still stages them for its other waves). On a
+    // wave's last tile the next-scores MFMAs read whatever the other K buffer
+    // holds and are discarded.
+    const int n_w = a.causal ? min(ntiles, q_last / kKTile + 1) : ntiles;
+    uint4 kst[2], vst[2];
+    fetch(kg, 0, kst);
+    fetch(vg, 0, vst);
+    put(sK[0], kKPad, kst);
+    put(sV[0], kVPad, vst);
+    if (ntiles > 1) {
+        fetch(kg, 1, kst);
+        put(sK[1], kKPad, kst);
+    }
     __syncthreads();
+    Scores sc = scores(0);
+    __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
     for (int j = 0; j < ntiles; ++j) {
-        const bool more = j + 1 < ntiles;
-        if (more) load_tile(j + 1);
-        const int key0 = j * kKTile;
-        // Wave-uniform: tiles wholly after this wave's queries are skipped;
-        // only tiles that reach the diagonal or the end of the keys are masked.
-        if (!(a.causal && key0 > q_last)) {
-            compute(j, j & 1, key0 + kKTile > N || (a.causal && key0 + kKTile - 1 > q0));
+        const bool more_k = j + 2 < ntiles;
+        const bool more_v = j + 1 < ntiles;
+        if (more_k) fetch(kg, j + 2, kst);
+        if (more_v) fetch(vg, j + 1, vst);
+        if (j < n_w) {
+            const bool masked = j * kKTile + kKTile > N || (a.causal && j * kKTile + kKTile - 1 > q0);
+            if (tile_max(j, sc, masked)) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
+            }
+            Scores next;
+            tile_pv(sc, j & 1, next, (j + 1) & 1);
+            sc = next;
         }
-        if (more) store_tile((j + 1) & 1);
+        if (more_k) put(sK[j & 1], kKPad, kst);
+        if (more_v) put(sV[(j + 1) & 1], kVPad, vst);
         __syncthreads();
     }
 
