@@ -11,6 +11,7 @@ timed with HIP events on the stream it runs on) and the float64 CPU oracle's
 throughput on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--sweep] [--no-cpu-baseline]
+  python bench.py --workload prefill_bf16_h32_n4096_causal   # the prefill kernel (TFLOP/s, matrix-core roofline)
   python bench.py --copy-probe BYTES   # a plain device copy, to scale rocprof byte counters
 """
 from __future__ import annotations
@@ -39,24 +40,32 @@ def log(msg: str) -> None:
     sys.stderr.flush()
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources: a committed counter profile is used only while it matches."""
+# The sources each timed kernel is built from (a counter profile is tied to them).
+KERNEL_SOURCES = {
+    "split_valu_kernel": ("fd_split_valu.hip", "fd_device.h", "fd_internal.h"),
+    "split_mfma_kernel": ("fd_split_mfma.hip", "fd_device.h", "fd_internal.h"),
+    "prefill_kernel": ("fd_prefill.hip", "fd_device.h", "fd_internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of one kernel's HIP sources: a committed counter profile is used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_13_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str) -> dict | None:
-    """HBM bytes per split-kernel launch from the committed rocprofv3 --pmc summary."""
+    """HBM bytes per launch of a kernel from the committed rocprofv3 --pmc summary."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(kernel):
         return None  # the kernel changed since the counters were taken
     return t
 
@@ -246,6 +255,105 @@ def _kv_elems(w, d) -> int:
     return (w.S if w.kind == "single" else int(d["total_kv"])) * w.Hkv * 128
 
 
+PREFILL_METRIC = "prefill attention TFLOP/s (useful flops: 4 * D per visible query-key pair and head)"
+PEAK_TFLOPS_16BIT = 2500.0  # MI355X dense bf16 / f16 matrix-core peak
+
+
+def bench_prefill(args) -> dict:
+    """One step = one fd_prefill call over the whole prompt batch (inputs resident in HBM)."""
+    import ctypes
+
+    import torch
+
+    import decode_attention_13_amd as fd
+    from decode_attention_13_amd.inputs import PREFILL_WORKLOADS
+    w = PREFILL_WORKLOADS[args.workload]
+    log(f"generating {w.name}")
+    d = w.make()
+    dev = torch.device("cuda:0")
+    q, k, v = d["q"].to(dev), d["k"].to(dev), d["v"].to(dev)
+    o = torch.empty_like(q)
+    lib = fd.lib()
+    code = fd.binding.FD_DTYPE[q.dtype]
+    stream = torch.cuda.current_stream()
+
+    def step(opt=None):
+        rc = lib.fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.N, w.H, w.Hkv, 128, code,
+                            d["scale"], int(w.causal), ctypes.byref(opt) if opt is not None else None,
+                            stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"{lib.fd_status_string(rc).decode()}: {lib.fd_last_error().decode()}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    begins = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for ev in begins + ends:
+        ev.record()
+    opts = [fd.options(split_begin_event=begins[i], split_end_event=ends[i]) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    for i in range(args.steps):
+        step(opts[i])
+    torch.cuda.synchronize()
+    ks = sorted(b.elapsed_time(e) / 1e3 for b, e in zip(begins, ends))
+    k_mean = sum(ks) / len(ks)
+    flops = w.flops()
+    traffic = load_traffic("prefill_kernel", w.name)
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "Hkv": w.Hkv, "D": 128, "causal": w.causal,
+                   "flops": flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / k_mean / 1e12, 2), "peak": PEAK_TFLOPS_16BIT,
+                     "unit": "TFLOP/s", "frac": round(flops / k_mean / 1e12 / PEAK_TFLOPS_16BIT, 4),
+                     "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
+                     "kernel": "prefill_kernel", "kernel_us_mean": round(k_mean * 1e6, 3),
+                     "kernel_us_median": round(ks[len(ks) // 2] * 1e6, 3), "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline_prefill(w, d)
+    return line
+
+
+def cpu_baseline_prefill(w, d, budget_s: float = 12.0) -> dict:
+    """The float64 oracle's prefill, one (sequence, head) at a time, over a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    n_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b, h = divmod(n_done % (w.B * w.H), w.H)
+        oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], w.causal, heads=[h], batches=[b])
+        n_done += 1
+    el = time.perf_counter() - t0
+    per_head = w.flops() / (w.B * w.H)
+    return {"value": round(per_head * n_done / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_done} (sequence, head) prefills of {w.name} (N={w.N}), {el:.1f} s"}
+
+
 def copy_probe(nbytes: int, steps: int) -> None:
     """A plain device-to-device copy of known size (for scaling FETCH_SIZE/WRITE_SIZE)."""
     import torch
@@ -285,7 +393,10 @@ def main() -> int:
         copy_probe(args.copy_probe, args.steps)
         return 0
 
-    from decode_attention_13_amd.inputs import WORKLOADS, sweep_workload
+    from decode_attention_13_amd.inputs import PREFILL_WORKLOADS, WORKLOADS, sweep_workload
+    if args.workload in PREFILL_WORKLOADS:
+        print(json.dumps(bench_prefill(args)), flush=True)
+        return 0
     w = WORKLOADS[args.workload]
     case = Case(w, args.chunk, args.kernel, kv=args.kv)
     split_kernel = SPLIT_KERNELS[case.plan["kernel"]]
