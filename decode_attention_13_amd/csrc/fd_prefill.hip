@@ -30,7 +30,9 @@ namespace fd {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;                 // waves per workgroup, 16 * QB queries each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPieces = 32 * 16 / kThreads;  // 16-byte pieces of a 32-key tile per thread
 constexpr int kKTile = 32;     // keys per LDS tile
 constexpr int kKPad = 272;     // LDS bytes per K row (256 + 16)
 constexpr int kVPad = 288;     // LDS bytes per V row (256 + 32, as for the transposed reads)
@@ -85,7 +87,7 @@ struct Mma<_Float16> {
 template <typename T, int QB>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     using M = Mma<T>;
-    constexpr int kQTile = 4 * 16 * QB;  // queries per workgroup
+    constexpr int kQTile = kWaves * 16 * QB;  // queries per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: wave-level branches stay scalar
     const int g = lane >> 4;
@@ -149,22 +151,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             }
     }
 
-    // Tile staging: thread t moves 16-byte pieces t and t + 256 of a K or V tile
+    // Tile staging: thread t moves 16-byte pieces t + i * kThreads of a K or V tile
     // (piece p: row p / 16, bytes (p % 16) * 16); rows past N re-read row N - 1.
     const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
     const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
     const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
-    auto fetch = [&](const char *src, int j, uint4 (&st)[2]) {
+    // A whole tile: a wave-uniform tile base plus a fixed 32-bit offset per lane.
+    uint32_t lane_off[kPieces];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = threadIdx.x + i * kThreads;
-            const int key = min(j * kKTile + (p >> 4), N - 1);
-            st[i] = load16(src + (size_t)key * tok_bytes + (p & 15) * 16);
+    for (int i = 0; i < kPieces; ++i) {
+        const int p = threadIdx.x + i * kThreads;
+        lane_off[i] = (uint32_t)(p >> 4) * (uint32_t)tok_bytes + (p & 15) * 16;
+    }
+    auto fetch = [&](const char *src, int j, uint4 (&st)[kPieces]) {
+        if (j * kKTile + kKTile <= N) {
+            const char *tile = src + (size_t)j * kKTile * tok_bytes;
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) st[i] = load16(tile + lane_off[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const int p = threadIdx.x + i * kThreads;
+                const int key = min(j * kKTile + (p >> 4), N - 1);
+                st[i] = load16(src + (size_t)key * tok_bytes + (p & 15) * 16);
+            }
         }
     };
-    auto put = [&](char *dst, int pad, const uint4 (&st)[2]) {
+    auto put = [&](char *dst, int pad, const uint4 (&st)[kPieces]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
             const int p = threadIdx.x + i * kThreads;
             *(lds_u32x4 *)(uintptr_t)(dst + (p >> 4) * pad + (p & 15) * 16) = u32x4{st[i].x, st[i].y, st[i].z, st[i].w};
         }
@@ -300,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     // wave's last tile the next-scores MFMAs read whatever the other K buffer
     // holds and are discarded.
     const int n_w = a.causal ? min(ntiles, q_last / kKTile + 1) : ntiles;
-    uint4 kst[2], vst[2];
+    uint4 kst[kPieces], vst[kPieces];
     fetch(kg, 0, kst);
     fetch(vg, 0, vst);
     put(sK[0], kKPad, kst);
@@ -354,11 +369,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
-constexpr int kQueryBlocks = 1;  // 16-query blocks per wave (2 costs occupancy and measured slower)
+constexpr int kQueryBlocks = 2;  // 16-query blocks per wave: each K / V fragment read from LDS feeds two
 
 hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     PrefillArgs arg = a;
-    arg.q_tiles = (a.N + 64 * kQueryBlocks - 1) / (64 * kQueryBlocks);
+    arg.q_tiles = (a.N + 16 * kWaves * kQueryBlocks - 1) / (16 * kWaves * kQueryBlocks);
     LaunchShape s{dim3(arg.q_tiles * a.H * a.B), dim3(kThreads)};
     void *args[] = {&arg};
     switch (dtype) {
