@@ -217,62 +217,58 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         return r;
     };
 
-    // Online softmax with a lazy running max: m moves only when a tile's max
-    // exceeds it by more than kLazyLog2 (P then stays below 2^kLazyLog2), so the
-    // accumulators are rescaled a few times per row instead of on most tiles.
-    // Any subtracted constant gives the same softmax; the final division uses the
-    // sum taken with the same constants.
-    //
-    // Step 1 (tile_max): mask the tile's scores, update m; returns whether the
-    // accumulators need rescaling (alpha holds the factors).
-    float alpha[QB], mu[QB];
-    auto tile_max = [&](int j, Scores &sc, bool masked) {
+    // Masked scores become -inf, so their P is exactly 0: keys at or past N,
+    // and with the causal mask keys after the query.
+    auto mask_scores = [&](int j, Scores &sc) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q_me = q0 + 16 * qb + c;
+            const int room = (a.causal ? min(q_me, N - 1) : N - 1) - j * kKTile - g * 4;  // key offset limit
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (sb * 16 + i > room) sc.v[qb][sb][i] = -INFINITY;
+        }
+    };
+
+    // Online softmax of one tile with a lazy running max: m moves only when the
+    // tile's max exceeds it by more than kLazyLog2 (P then stays below
+    // 2^kLazyLog2), so the accumulators are rescaled a few times per row instead
+    // of on most tiles. Any subtracted constant gives the same softmax; the final
+    // division uses the sum taken with the same constants. Produces P^T in the
+    // MFMA operand layout (bf16: hi and lo parts) and alpha, the factor for the
+    // accumulators; returns whether any row needs it.
+    struct Probs {
+        uint4 hi[QB], lo[QB];
+    };
+    float alpha[QB];
+    auto softmax = [&](const Scores &sc, Probs &pr) {
         bool rescale = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if (masked) {  // wave-uniform; masked scores become -inf, so their P is exactly 0
-                const int q_me = q0 + 16 * qb + c;
-                const int room = (a.causal ? min(q_me, N - 1) : N - 1) - j * kKTile - g * 4;  // key offset limit
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (sb * 16 + i > room) sc.v[qb][sb][i] = -INFINITY;
-            }
             const f32x4 s0 = sc.v[qb][0], s1 = sc.v[qb][1];
             // Raw-score max (the scale is > 0: its sign was moved into Q); med3
             // with +inf is a max that needs no NaN canonicalisation of its inputs.
             float mt = max2(max2(max2(s0[0], s0[1]), max2(s0[2], s0[3])), max2(max2(s1[0], s1[1]), max2(s1[2], s1[3])));
-            LanePair pr = lane_pair<16>(mt);
-            mt = max2(pr.lo, pr.hi);
-            pr = lane_pair<32>(mt);
-            mt = max2(pr.lo, pr.hi);
+            LanePair lp = lane_pair<16>(mt);
+            mt = max2(lp.lo, lp.hi);
+            lp = lane_pair<32>(mt);
+            mt = max2(lp.lo, lp.hi);
             const float mt_s = mt * sl;  // -inf stays -inf
             const float m_old = m[qb];
             const float m_new = mt_s > m_old + kLazyLog2 ? mt_s : m_old;
-            mu[qb] = finite_or_zero(m_new);
-            alpha[qb] = exp2_fast(m_old - mu[qb]);  // 0 while m_old is -inf
+            const float mu = finite_or_zero(m_new);
+            alpha[qb] = exp2_fast(m_old - mu);  // 0 while m_old is -inf
             rescale |= m_new != m_old && m_old > -INFINITY;
             m[qb] = m_new;
-        }
-        return __builtin_amdgcn_ballot_w64(rescale) != 0;
-    };
-
-    // Step 2 (tile_pv): P = exp2(s * sl - mu) and O^T += V^T . P^T from the V
-    // buffer; while the VALU forms P the matrix cores take the scores of the next
-    // tile (the scores MFMAs do not wait for P).
-    auto tile_pv = [&](const Scores &sc, int vbuf, Scores &next, int kbuf_next) {
-        next = scores(kbuf_next);
-        uint4 ph[QB], pl[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
             float pe[8];
             float ps = 0.f;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pe[sb * 4 + i] = exp2_fast(__builtin_fmaf(sc.v[qb][sb][i], sl, -mu[qb]));
+                    pe[sb * 4 + i] = exp2_fast(__builtin_fmaf(sc.v[qb][sb][i], sl, -mu));
                     ps += pe[sb * 4 + i];
                 }
             lsum[qb] = __builtin_fmaf(lsum[qb], alpha[qb], ps);
@@ -283,9 +279,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                 if constexpr (M::kSplitP)
                     lw[e2] = M::pack2(pe[2 * e2] - M::lo_of(hw[e2]), pe[2 * e2 + 1] - M::hi_of(hw[e2]));
             }
-            ph[qb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            if constexpr (M::kSplitP) pl[qb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            pr.hi[qb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if constexpr (M::kSplitP) pr.lo[qb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
+        return __builtin_amdgcn_ballot_w64(rescale) != 0;
+    };
+    auto rescale_acc = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
+    };
+
+    // O^T += V^T . P^T from a V buffer.
+    auto pv = [&](int vbuf, const Probs &pr) {
         lds_char *vt = (lds_char *)(uintptr_t)sV[vbuf];
         const int e = c >> 2, bq = c & 3;
 #pragma unroll
@@ -300,24 +307,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                acc[qb][db] = M::mma(va, ph[qb], acc[qb][db]);
-                if constexpr (M::kSplitP) acc[qb][db] = M::mma(va, pl[qb], acc[qb][db]);
+                acc[qb][db] = M::mma(va, pr.hi[qb], acc[qb][db]);
+                if constexpr (M::kSplitP) acc[qb][db] = M::mma(va, pr.lo[qb], acc[qb][db]);
             }
         }
     };
 
-    // Software pipeline: the K ring runs one tile ahead of the V ring, so the
-    // scores of tile j + 1 are formed while tile j's P is. Iteration j fetches
-    // K(j + 2) and V(j + 1) from global memory and stores them, after its own
-    // LDS reads, into the buffers that iteration j - 1 finished reading.
+    // Software pipeline, three tiles deep: iteration j runs P.V of tile j and the
+    // scores of tile j + 2 on the matrix cores while the VALU takes the softmax
+    // of tile j + 1 (none of the three waits for another). K runs two tiles ahead
+    // of V: iteration j fetches K(j + 3) and V(j + 1) from global memory and
+    // stores them, after its own LDS reads, into the buffers that iteration
+    // j - 1 finished reading; one barrier per tile.
     // Tiles this wave computes: with the causal mask those after its last query
-    // are skipped (the workgroup still stages them for its other waves). On a
-    // wave's last tile the next-scores MFMAs read whatever the other K buffer
-    // holds and are discarded.
+    // are skipped (the workgroup still stages them for its other waves). Scores
+    // formed past a wave's last tile read whatever the K buffer holds and are
+    // never used.
     const int n_w = a.causal ? min(ntiles, q_last / kKTile + 1) : ntiles;
-    uint4 kst[kPieces], vst[kPieces];
+    auto masked = [&](int j) { return j * kKTile + kKTile > N || (a.causal && j * kKTile + kKTile - 1 > q0); };
+    uint4 kst[kPieces], vst[kPieces], k2st[kPieces];
     fetch(kg, 0, kst);
     fetch(vg, 0, vst);
+    if (ntiles > 2) fetch(kg, 2, k2st);
     put(sK[0], kKPad, kst);
     put(sV[0], kVPad, vst);
     if (ntiles > 1) {
@@ -325,26 +336,38 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         put(sK[1], kKPad, kst);
     }
     __syncthreads();
-    Scores sc = scores(0);
-    __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
+    Scores sc0 = scores(0);
+    Scores sc1 = scores(1);  // tile 1, or discarded
+    __syncthreads();         // every wave has read K buffer 0
+    if (ntiles > 2) put(sK[0], kKPad, k2st);
+    if (masked(0)) mask_scores(0, sc0);
+    Probs p_cur;
+    softmax(sc0, p_cur);  // m starts at -inf: nothing to rescale
+    bool rescale = false;  // alpha of the last softmax applies before the next P.V
+    __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
-        const bool more_k = j + 2 < ntiles;
+        const bool more_k = j + 3 < ntiles;
         const bool more_v = j + 1 < ntiles;
-        if (more_k) fetch(kg, j + 2, kst);
+        if (more_k) fetch(kg, j + 3, kst);
         if (more_v) fetch(vg, j + 1, vst);
-        if (j < n_w) {
-            const bool masked = j * kKTile + kKTile > N || (a.causal && j * kKTile + kKTile - 1 > q0);
-            if (tile_max(j, sc, masked)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
-            }
-            Scores next;
-            tile_pv(sc, j & 1, next, (j + 1) & 1);
-            sc = next;
+        if (rescale) {  // softmax(j) moved m: before P.V(j)
+            rescale_acc();
+            rescale = false;
         }
-        if (more_k) put(sK[j & 1], kKPad, kst);
+        if (j + 1 < n_w) {
+            if (masked(j + 1)) mask_scores(j + 1, sc1);
+            Probs p_next;
+            // One block for the scheduler: P.V(j) and scores(j + 2) on the matrix
+            // cores, softmax(j + 1) on the VALU.
+            pv(j & 1, p_cur);
+            const Scores sc2 = scores(j & 1);
+            rescale = softmax(sc1, p_next);
+            sc1 = sc2;
+            p_cur = p_next;
+        } else if (j < n_w) {
+            pv(j & 1, p_cur);
+        }
+        if (more_k) put(sK[(j + 1) & 1], kKPad, kst);
         if (more_v) put(sV[(j + 1) & 1], kVPad, vst);
         __syncthreads();
     }
