@@ -195,6 +195,18 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
             "split_median_s": split_ms[len(split_ms) // 2] / 1e3}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float = 12.0, fp8: bool = False) -> dict:
     """The float64 oracle as it stands, timed on this host over a bounded sample
     (the E4M3 form of the oracle when the cache is FP8)."""
@@ -246,7 +258,7 @@ def cpu_baseline(w, budget_s: float = 12.0, fp8: bool = False) -> dict:
         sample = f"{n_done} whole sequences (all {w.H} heads) of {w.name}, {el:.1f} s"
         step_s = el / tokens_done * float(lens.sum())
     kv_bytes = 2 * _kv_elems(w, d) if fp8 else w.kv_bytes()  # E4M3: one byte per element
-    return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads, "cpu": cpu_model(), "kind": "oracle",
             "sample": sample, "us_per_step": round(step_s * 1e6, 1)}
 
 
@@ -350,7 +362,8 @@ def cpu_baseline_prefill(w, d, budget_s: float = 12.0) -> dict:
         n_done += 1
     el = time.perf_counter() - t0
     per_head = w.flops() / (w.B * w.H)
-    return {"value": round(per_head * n_done / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(per_head * n_done / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n_done} (sequence, head) prefills of {w.name} (N={w.N}), {el:.1f} s"}
 
 
