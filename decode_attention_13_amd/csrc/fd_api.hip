@@ -449,6 +449,7 @@ fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B
         return fail(FD_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
     if (N < 0) return fail(FD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
     if (N > (1 << 30)) return fail(FD_ERR_UNSUPPORTED, "N must be <= 2^30 (got %d)", N);
+    if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale must be finite");
     if (B > 65535 || H > 65535) return fail(FD_ERR_UNSUPPORTED, "B and H must be <= 65535");
     if ((long long)B * H * ((N + 63) / 64) > INT_MAX)
         return fail(FD_ERR_UNSUPPORTED, "B * H * ceil(N / 64) must fit in 31 bits");

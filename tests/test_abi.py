@@ -199,3 +199,27 @@ def test_no_device_is_reported():
     with pytest.raises(fd.FdError) as e:
         fd.decode_plan(8, 8, 512, "f32", 0)
     assert e.value.name == "FD_ERR_DEVICE"
+
+
+def test_prefill_rejects_bad_arguments_without_a_device():
+    lib = fd.lib()
+
+    def call(q=16, k=16, v=16, o=16, B=1, N=64, H=8, Hkv=2, D=128, dtype=2, scale=0.1, causal=1, opt=None):
+        return lib.fd_prefill(q, k, v, o, B, N, H, Hkv, D, dtype, scale, causal, opt, None)
+
+    assert "fd_prefill" in declared_functions()
+    assert call(N=0, q=None) == 0  # nothing to do: no launch, no pointer use
+    assert call(q=None) == 1
+    assert call(o=8) == 1  # misaligned
+    assert call(N=-1) == 1
+    assert call(H=6, Hkv=4) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(D=64) == 2
+    for code in (0, 3, 4, 7):  # f32, E4M3 caches, unknown
+        assert call(dtype=code) == 2
+    assert call(N=(1 << 30) + 1) == 2
+    assert call(B=65536) == 2
+    assert call(B=65535, H=65535, Hkv=65535, N=64) == 2  # grid beyond 31 bits
+    assert lib.fd_status_string(call(opt=ctypes.byref(fd.options(force_chunk=100)))).decode() == "FD_ERR_INVALID_ARG"
+    assert call(scale=float("nan")) == 1 and "scale" in lib.fd_last_error().decode()
