@@ -9,20 +9,19 @@
 // by element. The FlashAttention-2 layout the page describes (each Q block its
 // own workgroup, waves split by query rows) is kept.
 //
-// Workgroup: 64 * QB queries of one head (4 waves x 16 QB), key tiles of 32 tokens
-// staged in LDS and shared by the 4 waves (double buffered: the next tile's
-// global loads are in flight while the current one is computed).
-// Per wave and tile, the matrix-core work is that of the decode kernel with
-// query rows in place of query heads:
+// Workgroup: 4 waves x 16 * QB queries of one (sequence, head); key tiles of 32
+// tokens staged in LDS (two K and two V buffers) and shared by the 4 waves.
+// Per wave, 16-query block and tile, the matrix-core work is that of the decode
+// kernel with query rows in place of query heads:
 //   S^T[key, q] = K[key, :] . Q[q, :]       two 16x16x32 MFMA chains of 4
 //   online softmax per query (column), log2 domain, fp32
 //   O^T[d, q] += V^T[d, key] . P^T[key, q]  eight 16x16x32 MFMAs (bf16: P split
 //       into two 16-bit parts, two MFMAs each, which keeps P.V near fp32)
+// The loop is a three-stage software pipeline: P.V of tile j and the scores of
+// tile j + 2 go to the matrix cores while the VALU takes the softmax of j + 1.
 // P^T needs no lane movement (key slot (l/16)*8 + j holds key
 // (j/4)*16 + (l/16)*4 + j%4, the keys of that lane's S accumulators); V^T comes
 // from the LDS tile with ds_read_b64_tr_b16.
-#include <type_traits>
-
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -30,10 +29,10 @@ namespace fd {
 
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup, 16 * QB queries each
+constexpr int kWaves = 4;      // waves per workgroup, 16 * QB queries each
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPieces = 32 * 16 / kThreads;  // 16-byte pieces of a 32-key tile per thread
 constexpr int kKTile = 32;     // keys per LDS tile
+constexpr int kPieces = kKTile * 16 / kThreads;  // 16-byte pieces (16 per 256-B row) of a tile per thread
 constexpr int kKPad = 272;     // LDS bytes per K row (256 + 16)
 constexpr int kVPad = 288;     // LDS bytes per V row (256 + 32, as for the transposed reads)
 constexpr int kXcds = 8;       // XCDs of the MI355X, each with its own L2
