@@ -134,3 +134,16 @@ def test_rising_scores_rescale_every_tile(dtype, device):
         torch.cuda.synchronize()
         ref, _ = oracle.prefill_attention(q, k, v, scale, causal)
         assert_close(o.cpu(), ref, f"rising {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("B,N,H,Hkv", [(1, 300, 6, 1), (3, 257, 12, 3), (2, 190, 16, 2), (1, 96, 1, 1)])
+def test_head_groupings(B, N, H, Hkv, device):
+    """MQA (one KV head), GQA 4 and 8, and a single head; (sequence, head) unit
+    counts that are and are not multiples of the XCD count, so both workgroup
+    orders of the grid run."""
+    d = inputs.prefill_inputs(B, N, H, Hkv, 128, "bf16", 550 + H)
+    for causal in (True, False):
+        announce(f"B={B} N={N} H={H}/{Hkv} causal={causal}")
+        o = run(d, device, causal)
+        ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
+        assert_close(o, ref, f"B={B} N={N} H={H}/{Hkv} causal={causal}")
