@@ -47,16 +47,20 @@ long long pow2_floor(long long x) {
 }
 
 // Planner constants (measured on MI355X).
-//  - Workgroups aimed at per compute unit (contiguous caches): a split-kernel
-//    workgroup is 4 waves, each with one or two tiles of K/V in flight, so a few
-//    resident workgroups per CU keep the HBM queues full.
 //  - Chunk bounds: long enough to amortise a workgroup's start (q load, first
 //    round trip to HBM) and its partial write, short enough to spread short
 //    caches over the chip.
-constexpr int kTargetWgsPerCu = 4;
-// With KV heads packed per workgroup (MHA), two workgroups per CU measured best
-// (4k and 128k tokens, bf16 and E4M3 caches): each reads hp rows per token.
-constexpr int kTargetWgsPerCuPacked = 2;
+// Workgroups aimed at per compute unit (contiguous caches). A split-kernel
+// workgroup is 4 waves, each with one or two K/V tiles in flight. Measured over
+// 2k-128k tokens: one workgroup per CU is best for MHA with two KV heads packed
+// (16-bit and fp32 rows) and for GQA on both kernels (16-bit, fp32 and E4M3
+// caches), by up to 15-30% at 8k-32k tokens; two are best for MHA over E4M3
+// rows (four KV heads packed, half the bytes per load) and for MHA caches
+// under 64 MiB.
+int target_wgs_per_cu(fd_dtype dtype, bool mha, long long kv_bytes) {
+    if (mha && (fd::is_fp8_cache(dtype) || kv_bytes < (64LL << 20))) return 2;
+    return 1;
+}
 // Paged batches: a workgroup pays a fixed cost (block-table and first KV round
 // trips, the end-of-split merge and partial store) worth about kWgFixedBytes of
 // streaming at its share of the bandwidth, and a ragged batch ends with about
@@ -158,7 +162,8 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
         const long long work = std::max(total, 1LL) * slices;
-        const long long target = (long long)num_cus * (hp > 1 ? kTargetWgsPerCuPacked : kTargetWgsPerCu);
+        const long long kv_bytes = std::max(total, 1LL) * Hkv * 2LL * FD_HEAD_DIM * cache_elem_bytes(dtype);
+        const long long target = (long long)num_cus * target_wgs_per_cu(dtype, H == Hkv, kv_bytes);
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
