@@ -403,12 +403,22 @@ __device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
     return split == n - 1 ? L : (split + 1) * chunk;
 }
 
-// ---------------------------------------------------------------- work list
-// Paged launches whose grid would be mostly empty splits (a batch far shorter
-// than its longest sequence) number the splits that hold tokens instead:
-// sequence b contributes max(1, splits_of(L_b)) items (one item writes the zeros
-// of an empty sequence), s_start[b] = items before b, s_start[B] = the total.
-// Every thread of the workgroup must call this (it holds barriers). B <= kMaxListSeqs.
+// ---------------------------------------------------------------- paged item order
+// Sequence b of a paged batch has n_b = max(1, splits_of(L_b)) items (one item
+// writes the zeros of an empty sequence). Its last split also takes the
+// remainder, so it holds chunk to 2*chunk - 1 tokens while the others hold
+// exactly chunk: the last splits are the largest items. Workgroups start in
+// linear-id order, so the items are numbered largest first: items 0 .. B-1 are
+// the last splits of sequences 0 .. B-1, then come the other splits, sequence
+// by sequence. The batch then ends on equal-sized items instead of a random
+// mix of sizes (the longest-first rule of list scheduling); the splits
+// themselves, and so the results, do not change.
+
+// Work list (a batch far shorter than its longest sequence, with total_kv
+// known): grid y numbers only items that exist. s_start[b] = the non-last
+// splits of sequences before b, s_start[B] = their total, which is returned.
+// Every thread of the workgroup must call this (it holds barriers).
+// B <= kMaxListSeqs.
 __device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start, int *s_wave) {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -418,7 +428,7 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start,
     for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
         const int bb = 4 * t + j;
         int n = 0;
-        if (bb < a.B) n = max(1, splits_of(max(0, min(a.seq_lens[bb], a.max_len)), a.chunk));
+        if (bb < a.B) n = max(1, splits_of(max(0, min(a.seq_lens[bb], a.max_len)), a.chunk)) - 1;
         cnt[j] = n;
         local += n;
     }
@@ -444,16 +454,29 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start,
     return s_start[a.B];
 }
 
-// The sequence of work item `item`: the largest b with s_start[b] <= item (every
-// sequence has at least one item, so s_start increases strictly).
-__device__ __forceinline__ int find_sequence(const int *s_start, int B, int item) {
+// The sequence of the r-th non-last split: the largest b with s_start[b] <= r.
+// s_start does not decrease, and a sequence with no such split shares its
+// start with the next one, so the largest such b is the one holding r.
+__device__ __forceinline__ int find_sequence(const int *s_start, int B, int r) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_start[mid] <= item) lo = mid;
+        if (s_start[mid] <= r) lo = mid;
         else hi = mid - 1;
     }
     return lo;
+}
+
+// (sequence, split) of work-list item `item` < B + s_start[B].
+__device__ __forceinline__ void work_list_item(const int *s_start, int B, int item, int &b, int &split) {
+    if (item < B) {
+        b = item;
+        split = s_start[b + 1] - s_start[b];  // the last split: index n_b - 1
+    } else {
+        const int r = item - B;
+        b = find_sequence(s_start, B, r);
+        split = r - s_start[b];
+    }
 }
 
 // When total_kv understated the batch, items past the grid have no workgroup.
@@ -464,9 +487,9 @@ template <typename T>
 __device__ void poison_unlisted(const SplitArgs &a, const int *s_start, int items) {
     const float nan = __builtin_nanf("");
     for (int item = a.grid_items; item < items; ++item) {
-        const int b = find_sequence(s_start, a.B, item);
-        const int n = s_start[b + 1] - s_start[b];
-        const int split = item - s_start[b];
+        int b, split;
+        work_list_item(s_start, a.B, item, b, split);
+        const int n = s_start[b + 1] - s_start[b] + 1;
         if (n == 1) {
             T *o = reinterpret_cast<T *>(a.out) + (size_t)b * a.H * kHeadDim;
             for (int i = threadIdx.x; i < a.H * kHeadDim; i += kSplitThreads) o[i] = Elem<T>::store_cast(nan);
@@ -475,6 +498,40 @@ __device__ void poison_unlisted(const SplitArgs &a, const int *s_start, int item
                 a.ws_lse[((size_t)b * a.H + h) * a.num_splits + split] = nan;
         }
     }
+}
+
+// The item of a paged workgroup, in the order above. With a work list, grid y
+// is the item number. Otherwise the (splits x sequences) plane of the grid is
+// read as one index u = y + num_splits * z: u < B is the last split of
+// sequence u (its index needs L_u first), and u - B = (num_splits - 1) * b + s
+// is split s of sequence b, which the workgroup skips unless s < n_b - 1
+// (*not_last = 1; splits past a sequence's end are the grid's empty slots).
+// Returns false when the workgroup has nothing to do. Every thread of the
+// workgroup must call this (the work list holds barriers).
+template <typename T>
+__device__ __forceinline__ bool paged_item(const SplitArgs &a, int *s_start, int *s_wave, int &b, int &split,
+                                           int &not_last) {
+    not_last = 0;
+    if (a.work_list) {
+        const int items = a.B + build_work_list(a, s_start, s_wave);
+        const int item = blockIdx.y;
+        if (item == a.grid_items - 1 && blockIdx.x == 0 && items > a.grid_items)
+            poison_unlisted<T>(a, s_start, items);  // total_kv was short: fail loudly
+        if (item >= items) return false;
+        work_list_item(s_start, a.B, item, b, split);
+        return true;
+    }
+    const int u = blockIdx.y + a.num_splits * blockIdx.z;
+    if (u < a.B) {
+        b = u;
+        split = max(1, splits_of(max(0, min(a.seq_lens[b], a.max_len)), a.chunk)) - 1;
+    } else {
+        const int v = u - a.B;  // only reached when num_splits > 1
+        b = v / (a.num_splits - 1);
+        split = v - b * (a.num_splits - 1);
+        not_last = 1;
+    }
+    return true;
 }
 
 // ---------------------------------------------------------------- split epilogue

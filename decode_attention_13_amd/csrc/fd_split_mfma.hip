@@ -148,7 +148,7 @@ struct KvFrag<T, fp8e4m3> {
 };
 
 template <typename T, typename KV, int MODE>
-__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b, const int split) {
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b, const int split, const int not_last) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
     using F = KvFrag<T, KV>;
@@ -173,8 +173,8 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
     int page_first = 0;
     const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
     const int n_b = splits_of(L, a.chunk);
-    if (split >= n_b) {  // uniform over the workgroup
-        if (split == 0) {  // empty sequence: o = 0
+    if (split >= n_b - not_last) {  // uniform over the workgroup
+        if (split == 0 && !not_last) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
@@ -393,28 +393,21 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
     });
 }
 
-// One workgroup per (head slice, split, sequence); with a work list (paged
-// batches much shorter than their longest sequence), the splits that hold
-// tokens are numbered sequence by sequence and workgroup y takes items y,
-// y + grid_items, ...: no workgroup is launched only to find its split empty.
+// One workgroup per (head slice, split, sequence). Paged batches take their
+// (sequence, split) items largest first, the last split of every sequence
+// before the others (paged_item); with a work list (a batch much shorter than
+// its longest sequence) grid y numbers only items that exist, so no workgroup
+// is launched only to find its split empty.
 template <typename T, typename KV, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
     pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
-    int b = blockIdx.z, split = blockIdx.y;
+    int b = blockIdx.z, split = blockIdx.y, not_last = 0;
     if constexpr (MODE != kContig) {
-        if (a.work_list) {
-            __shared__ int s_start[kMaxListSeqs + 1];
-            __shared__ int s_wave[kSplitThreads / 64];
-            const int items = build_work_list(a, s_start, s_wave);
-            const int item = blockIdx.y;
-            if (item == a.grid_items - 1 && blockIdx.x == 0 && items > a.grid_items)
-                poison_unlisted<T>(a, s_start, items);  // total_kv was short: fail loudly
-            if (item >= items) return;
-            b = find_sequence(s_start, a.B, item);
-            split = item - s_start[b];
-        }
+        __shared__ int s_start[kMaxListSeqs + 1];
+        __shared__ int s_wave[kSplitThreads / 64];
+        if (!paged_item<T>(a, s_start, s_wave, b, split, not_last)) return;
     }
-    split_mfma_item<T, KV, MODE>(a, b, split);
+    split_mfma_item<T, KV, MODE>(a, b, split, not_last);
 }
 
 template <typename T, typename KV, int MODE>

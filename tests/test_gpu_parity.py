@@ -481,9 +481,12 @@ def test_work_list_short_total_is_nan(device):
     short = sum(lens) // 3
     plan = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), short, 0, opt)
     assert plan["work_list"] == 1
-    counts = [max(1, L // 256) for L in lens]
-    start = np.concatenate([[0], np.cumsum(counts)])
-    missing = [b for b in range(48) if start[b + 1] > plan["grid_y"]]
+    # Items: the last split of each of the 48 sequences first, then the other
+    # splits sequence by sequence; the grid holds the first grid_y of them.
+    others = [max(1, L // 256) - 1 for L in lens]
+    start = 48 + np.concatenate([[0], np.cumsum(others)])
+    assert plan["grid_y"] >= 48
+    missing = [b for b in range(48) if others[b] > 0 and start[b + 1] > plan["grid_y"]]
     assert missing and len(missing) < 48
     g = to_dev(d, device)
     outs = []
