@@ -7,10 +7,12 @@ The KV cache is rotated over enough device copies that every step reads it cold
 
 Printed: one JSON line with the metric, the whole-step throughput (unique K+V
 bytes / step time), the dominant kernel's roofline (its own launch durations
-timed with HIP events on the stream it runs on) and the float64 CPU oracle's
-throughput on a bounded sample of the same workload.
+timed with HIP events on the stream it runs on), the float64 CPU oracle's
+throughput on a bounded sample of the same workload and, for single-sequence
+decode workloads, the KV-length curve the metric is stated over (32 heads,
+S = 4k .. 128k and 131073 tokens; "sweep").
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--sweep] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--no-sweep] [--no-cpu-baseline]
   python bench.py --workload prefill_bf16_h32_n4096_causal   # the prefill kernel (TFLOP/s, matrix-core roofline)
   python bench.py --copy-probe BYTES   # a plain device copy, to scale rocprof byte counters
 """
@@ -388,7 +390,9 @@ def main() -> int:
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"], help="force the split kernel")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="cache storage: the workload's dtype, or FP8 E4M3 codes with per-tensor scales")
-    ap.add_argument("--sweep", action="store_true", help="also time the pages' KV-length sweep (4k..128k)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the pages' KV-length sweep (4k..128k) also for a paged workload")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the KV-length sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
@@ -447,7 +451,7 @@ def main() -> int:
     case_fp8 = case.fp8
     del case
     torch.cuda.empty_cache()
-    if args.sweep:
+    if (args.sweep or w.kind == "single") and not args.no_sweep:
         sweep = []
         for S in SWEEP:
             c = Case(sweep_workload(S), kv=args.kv)
