@@ -99,10 +99,10 @@ typedef struct fd_plan {
                                H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
     size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
-    int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens, sequence by
-                               sequence, grid_z = 1, and workgroup y takes items y, y + grid_y, ...;
-                               chosen when the (splits x sequences) grid would be mostly empty splits
-                               and total_kv is known */
+    int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens (the last
+                               split of every sequence first, then the others sequence by sequence),
+                               grid_z = 1, one split per workgroup; chosen when the (splits x
+                               sequences) grid would be mostly empty splits and total_kv is known */
     int reserved2;
 } fd_plan;
 
@@ -218,7 +218,6 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
                                 int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
                                 void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
 
-/* Static name of a status code. */
 /*
  * Prefill attention: many queries over a prompt, optionally causal
  * ("FlashAttention 与推理算子", sections "标准注意力的问题" and
@@ -241,6 +240,7 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
 fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B, int N, int H, int Hkv, int D,
                      fd_dtype dtype, float scale, int causal, const fd_options *opt, void *stream);
 
+/* Static name of a status code. */
 const char *fd_status_string(fd_status s);
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -509,3 +509,32 @@ def test_workspace_too_small_is_rejected(device):
     with pytest.raises(fd.FdError) as e:
         fd.fd_decode(d["q"], d["k"], d["v"], scale=0.1, ws=ws, opt=fd.options(force_num_splits=4))
     assert e.value.name == "FD_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_paged_largest_work_list_batch(B, device):
+    """The work list holds at most 1024 sequences (their offsets live in LDS): a
+    batch of 1024 short ragged sequences takes it, 1025 falls back to the grid.
+    Both match the oracle on sampled rows, the last sequences included, and the
+    1024-sequence batch is bit-identical to its own full-grid run."""
+    rng = np.random.default_rng(900 + B)
+    lens = np.clip(np.round(np.exp(rng.uniform(0.0, np.log(2000), B))), 1, 2000).astype(int).tolist()
+    d = inputs.paged_inputs(B, 8, 2, 128, "bf16", 16, lens, 901 + B)
+    opt = fd.options(force_chunk=64)
+    total = sum(lens)
+    plan = fd.paged_plan(B, 8, 2, "bf16", 16, max(lens), total, 0, opt)
+    assert plan["work_list"] == (1 if B <= 1024 else 0)
+    announce(f"paged largest work-list batch B={B}")
+    o = run_paged(d, device, opt=opt)
+    bs = sorted(set(list(range(0, B, 97)) + [B - 2, B - 1]))
+    pairs = [(b, h) for b in bs for h in (0, 7)]
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"], pairs=pairs)
+    assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, "bf16", f"B={B}")
+    if plan["work_list"]:
+        g = to_dev(d, device)
+        announce(f"paged largest work-list batch B={B}, full grid")
+        og = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                                scale=d["scale"], max_seq_len=max(lens), total_kv=0, opt=opt)
+        torch.cuda.synchronize()
+        assert torch.equal(o.cpu(), og.cpu())
