@@ -65,9 +65,15 @@ int target_wgs_per_cu(fd_dtype dtype, bool mha, long long kv_bytes) {
 // trips, the end-of-split merge and partial store) worth about kWgFixedBytes of
 // streaming at its share of the bandwidth, and a ragged batch ends with about
 // half a workgroup of imbalance per resident slot. Balancing the two terms gives
-// a workgroup size of sqrt(2 * bytes per slot * kWgFixedBytes). Measured on the
-// GQA4 and GQA8 batches (bf16/f16 and E4M3 caches): best strides 1024 and 2048.
+// a workgroup size of sqrt(2 * bytes per slot * kWgFixedBytes). A work-list
+// workgroup first loads every sequence length and numbers the items (a prefix
+// sum and two barriers) before it can load its table slice: one more dependent
+// round trip, and a larger fixed cost. Measured on the GQA4 batch (grid) and
+// the GQA8 batch (work list), bf16/f16 and E4M3 caches, with the largest items
+// started first: best strides 1024 and 4096 (2048 for the GQA8 batch cost 2.2%
+// on the 16-bit cache and 2.5% on the E4M3 cache).
 constexpr double kWgFixedBytes = 32768.0;
+constexpr double kWgFixedBytesList = 3.0 * kWgFixedBytes;
 constexpr int kPagedSlotsPerCu = 2;  // resident split workgroups per CU (two waves per SIMD)
 constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 16384;
@@ -126,7 +132,19 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
     return FD_OK;
 }
 
-// Shared planner. `max_len` is the longest sequence, `total` the sum of the
+// Whether a paged launch numbers its items (work list): sequence b has at most
+// 1 + L_b / chunk splits, so a known total bounds the items by B + total / chunk.
+// When the full (splits x sequences) grid would be more than twice that, the
+// launch holds that many workgroups instead. An understated total_kv leaves
+// items without a workgroup; their outputs become NaN.
+bool uses_work_list(int B, int max_len, long long total, bool total_known, long long chunk) {
+    if (!total_known || B <= 1 || B > fd::kMaxListSeqs) return false;
+    const long long splits = std::max(1LL, (long long)max_len / chunk);
+    const long long items = (long long)B + total / chunk;
+    return (long long)B * splits >= 2 * items;
+}
+
+// Shared planner.// Shared planner. `max_len` is the longest sequence, `total` the sum of the
 // lengths (one sequence for contiguous decode), `page_size` 0 when contiguous.
 fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long long total, bool total_known,
                     int page_size, int num_cus, const fd_options *opt, fd_plan *p) {
@@ -155,9 +173,16 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         const double row_bytes = 2.0 * FD_HEAD_DIM * cache_elem_bytes(dtype) * hp;  // K + V of one token, per workgroup
         const double per_slot =
             (double)std::max(total, 1LL) * (Hkv / hp) * row_bytes / ((double)num_cus * kPagedSlotsPerCu);
-        const double tokens = std::sqrt(2.0 * per_slot * kWgFixedBytes) / row_bytes;
-        chunk = 1LL << std::max(0L, std::lround(std::log2(std::max(tokens, 1.0))));  // nearest power of two
-        chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
+        auto balanced = [&](double fixed_bytes) {
+            const double tokens = std::sqrt(2.0 * per_slot * fixed_bytes) / row_bytes;
+            const long long c = 1LL << std::max(0L, std::lround(std::log2(std::max(tokens, 1.0))));  // nearest power of two
+            return std::min<long long>(std::max<long long>(c, kMinChunk), kMaxChunk);
+        };
+        chunk = balanced(kWgFixedBytes);
+        if (uses_work_list(B, max_len, total, total_known, chunk)) {
+            const long long c = balanced(kWgFixedBytesList);
+            if (uses_work_list(B, max_len, total, total_known, c)) chunk = c;
+        }
     } else {
         // Token-rows over all workgroups divided by the workgroups wanted,
         // rounded down to a power of two, then clamped.
@@ -205,18 +230,11 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     p->threads = 256;
     p->merge = splits > 1 ? 1 : 0;
     p->kv_heads_per_group = hp;
-    // Work list: sequence b has at most 1 + L_b / chunk splits, so a known total
-    // bounds the items by B + total / chunk. When the full grid would be more
-    // than twice that, launch that many workgroups instead. An understated
-    // total_kv leaves items without a workgroup; their outputs become NaN.
-    if (page_size > 0 && total_known && B > 1 && B <= fd::kMaxListSeqs) {
-        const long long items = (long long)B + total / chunk;
-        const long long full = (long long)B * splits;
-        if (full >= 2 * items) {
-            p->work_list = 1;
-            p->grid_y = (int)std::min(items, full);
-            p->grid_z = 1;
-        }
+    // Work list (uses_work_list): grid y numbers the items that exist.
+    if (page_size > 0 && uses_work_list(B, max_len, total, total_known, chunk)) {
+        p->work_list = 1;
+        p->grid_y = (int)std::min((long long)B + total / chunk, (long long)B * splits);
+        p->grid_z = 1;
     }
     if (p->merge) {
         const size_t rows = (size_t)B * H * splits;
