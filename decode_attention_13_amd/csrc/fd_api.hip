@@ -345,11 +345,21 @@ fd_status check_scales(float k_scale, float v_scale) {
     return FD_OK;
 }
 
+// The kernels take the scores in the log2 domain: scale * k_scale * log2(e) must
+// be a finite float (an infinite one would turn every exponent into inf - inf).
+fd_status check_score_scale(float scale, float k_scale) {
+    if (!std::isfinite(scale) || !std::isfinite(scale * k_scale * fd::kLog2eHost))
+        return fail(FD_ERR_INVALID_ARG, "scale must be finite (scale * k_scale * log2(e) = %g)",
+                    (double)(scale * k_scale * fd::kLog2eHost));
+    return FD_OK;
+}
+
 fd_status decode_impl(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
                       fd_dtype dtype, float scale, float k_scale, float v_scale, void *ws, size_t ws_bytes,
                       const fd_options *opt, void *stream) {
     fd_status s = check_common(1, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
+    if ((s = check_score_scale(scale, k_scale)) != FD_OK) return s;
     if (S < 0) return fail(FD_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
     if (!q || !o || (S > 0 && (!k || !v))) return fail(FD_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -381,6 +391,7 @@ fd_status paged_impl(const void *q, const void *k_cache, const void *v_cache, co
                      fd_dtype dtype, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
     fd_status s = check_common(B, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
+    if ((s = check_score_scale(scale, k_scale)) != FD_OK) return s;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
         return fail(FD_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and o must not be NULL");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))

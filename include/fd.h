@@ -149,7 +149,9 @@ fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_s
  *   k  [S, Hkv, D]     keys, token-major
  *   v  [S, Hkv, D]     values, token-major
  *   o  [H, D]          output, fully overwritten (S == 0 gives zeros)
- *   scale              softmax scale (callers usually pass 1/sqrt(D))
+ *   scale              softmax scale (callers usually pass 1/sqrt(D)); any finite value,
+ *                      negative and zero included, whose product with log2(e) (and
+ *                      k_scale, for an FP8 cache) is finite, else FD_ERR_INVALID_ARG
  *   ws, ws_bytes       caller-owned device workspace of at least
  *                      fd_plan.workspace_bytes (may be NULL when that is 0)
  *   opt                NULL or options; stream: hipStream_t or NULL.

@@ -159,6 +159,21 @@ def test_decode_rejects_bad_pointers_without_a_device():
     assert lib.fd_status_string(rc).decode() == "FD_ERR_INVALID_ARG"  # misaligned block table
 
 
+def test_decode_rejects_a_non_finite_scale_without_a_device():
+    """The scores are scaled by scale * k_scale * log2(e) in fp32: a non-finite scale,
+    or a product that overflows, is refused before anything is launched."""
+    lib = fd.lib()
+    for scale, ks in ((float("nan"), 1.0), (float("inf"), 1.0), (-float("inf"), 1.0), (3e38, 1.0), (1e30, 1e30)):
+        if ks == 1.0:
+            assert lib.fd_decode(16, 16, 16, 32, 8, 8, 512, 128, 2, scale, None, 0, None, None) == 1
+            assert "scale" in lib.fd_last_error().decode()
+            assert lib.fd_paged_decode(16, 16, 16, 16, 16, 16, 16, scale, 2, 8, 8, 128, 4, 4, 64, 0, 2, None, 0,
+                                       None, None) == 1
+        assert lib.fd_decode_fp8kv(16, 16, 16, 32, 8, 8, 512, 128, 4, scale, ks, 1.0, None, 0, None, None) == 1
+        assert lib.fd_paged_decode_fp8kv(16, 16, 16, 16, 16, 16, 16, scale, ks, 1.0, 2, 8, 8, 128, 4, 4, 64, 0, 4,
+                                         None, 0, None, None) == 1
+
+
 def test_fp8_cache_plans_and_dtype_routing():
     # E4M3 caches plan like their query type (same kernel choice and split shape),
     # except that MHA packs 4 KV heads (128-B rows) per workgroup instead of 2

@@ -343,7 +343,7 @@ def _pools(lens, Hkv, ps, dtype, seed):
 
 
 @pytest.mark.parametrize("kernel", ["auto", "valu"])
-@pytest.mark.parametrize("ps", [1, 16, 64, 256])
+@pytest.mark.parametrize("ps", [1, 4, 16, 64, 256, 1024])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_paged_addressing_is_bit_exact(ps, dtype, kernel, device):
     """Shuffled table over a scattered pool == identity table over in-order pages, bit
@@ -538,3 +538,33 @@ def test_paged_largest_work_list_batch(B, device):
                                 scale=d["scale"], max_seq_len=max(lens), total_kv=0, opt=opt)
         torch.cuda.synchronize()
         assert torch.equal(o.cpu(), og.cpu())
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (32, 4)])
+@pytest.mark.parametrize("scale", [float(np.float32(-0.3)), 0.0, float(np.float32(2.5))])
+def test_decode_any_finite_scale(H, Hkv, scale, device):
+    """The online softmax takes scores of any sign and size: a negative scale, a
+    zero one (every weight equal: the mean of V) and a large one (a peaked
+    softmax), on both split kernels (MHA on the vector ALUs, GQA4 on the matrix
+    cores) and through the block table."""
+    d = inputs.single_inputs(H, Hkv, 1000, 128, "bf16", 520 + H)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], scale)
+    g = to_dev(d, device)
+    for kernel in ("auto", "valu"):
+        announce(f"decode scale={scale} H={H} Hkv={Hkv} {kernel}")
+        o = fd.fd_decode(g["q"], g["k"], g["v"], scale=scale, opt=fd.options(force_chunk=256, kernel=kernel))
+        torch.cuda.synchronize()
+        assert_close(o, ref, "bf16", f"scale={scale} {kernel}")
+    # the same tokens as one paged sequence (pages of 16 in order)
+    pages = -(-1000 // 16)
+    kp = torch.zeros(pages * 16, Hkv, 128, dtype=d["k"].dtype)
+    vp = torch.zeros_like(kp)
+    kp[:1000], vp[:1000] = d["k"], d["v"]
+    table = torch.arange(pages, dtype=torch.int32).reshape(1, pages)
+    announce(f"paged decode scale={scale} H={H} Hkv={Hkv}")
+    o = fd.fd_paged_decode(g["q"].reshape(1, H, 128), kp.reshape(pages, 16, Hkv, 128).to(device),
+                           vp.reshape(pages, 16, Hkv, 128).to(device), table.to(device),
+                           torch.tensor([1000], dtype=torch.int32, device=device), 16, scale=scale,
+                           max_seq_len=1000, total_kv=1000, opt=fd.options(force_chunk=256))
+    torch.cuda.synchronize()
+    assert_close(o[0], ref, "bf16", f"paged scale={scale}")
