@@ -152,8 +152,8 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b,
                     (uint32_t)(min(t0 + r * kTok, t_end - 1) - tb) * (uint32_t)A.token_bytes + (uint32_t)row_off;
 #pragma unroll
                 for (int pc = 0; pc < NL; ++pc) {
-                    kx[r][pc] = R::load(kb + off + R::offset(c, pc) * sizeof(KV));
-                    vx[r][pc] = R::load(vb + off + R::offset(c, pc) * sizeof(KV));
+                    kx[r][pc] = R::load_at(kb, off + R::offset(c, pc) * sizeof(KV));
+                    vx[r][pc] = R::load_at(vb, off + R::offset(c, pc) * sizeof(KV));
                 }
             }
         }
