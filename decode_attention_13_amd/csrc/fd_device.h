@@ -139,7 +139,8 @@ __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cas
 // global form on the 32-head bf16 decode: 1.7% faster at 128k tokens, 1.5% at
 // 4k (the nt, sc0, sc1 policy bits made no difference). Used for 16-bit rows;
 // fp32 rows measured the same either way and 8-byte E4M3 rows slower, so
-// those keep the global form.
+// those keep the global form. stream_rsrc also serves the prefill kernel's
+// whole-tile fetches (temporal there: every query tile of a head re-reads them).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *uniform_base) {
     const uint64_t a = reinterpret_cast<uint64_t>(uniform_base);
     const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |

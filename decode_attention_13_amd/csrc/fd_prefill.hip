@@ -164,9 +164,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
     auto fetch = [&](const char *src, int j, uint4 (&st)[kPieces]) {
         if (j * kKTile + kKTile <= N) {
-            const char *tile = src + (size_t)j * kKTile * tok_bytes;
+            // buffer loads from the uniform tile base (2% on the f16 GQA workload)
+            const __amdgpu_buffer_rsrc_t r = stream_rsrc(src + (size_t)j * kKTile * tok_bytes);
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) st[i] = load16(tile + lane_off[i]);
+            for (int i = 0; i < kPieces; ++i) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off[i], 0, 0);
+                st[i] = make_uint4(x.x, x.y, x.z, x.w);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < kPieces; ++i) {
