@@ -111,6 +111,24 @@ def test_plan_work_list_choice():
     assert fd.paged_plan(64, 32, 8, "bf16", 16, 8192, 64 * 8192, 256)["work_list"] == 0
 
 
+def test_plan_paged_strides_of_the_batches():
+    """The paged balance (per-workgroup fixed cost against the ragged tail, three
+    times the fixed cost when the work list is taken) picks 1024 tokens on the
+    full grid for the GQA4 batch and 4096 on the work list for the GQA8 batch,
+    for 16-bit and E4M3 caches alike; with an unknown total (taken as B times
+    the longest sequence) the GQA8 batch runs on the full grid."""
+    for name, chunk, wl in (("paged_gqa4_bf16_b64_s1k-8k", 1024, 0), ("paged_gqa8_f16_b128_s256-64k", 4096, 1)):
+        w = WORKLOADS[name]
+        L = w.seq_lens()
+        for dt in (w.dtype, f"{w.dtype}_kv_e4m3"):
+            p = fd.paged_plan(w.B, w.H, w.Hkv, dt, w.page_size, int(L.max()), int(L.sum()), 256)
+            assert (p["chunk"], p["work_list"]) == (chunk, wl), (name, dt, p)
+    w = WORKLOADS["paged_gqa8_f16_b128_s256-64k"]
+    L = w.seq_lens()
+    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256)
+    assert p["work_list"] == 0 and p["grid_z"] == w.B
+
+
 def test_plan_paged_chunk_fits_block_table_stage():
     for ps in (1, 2, 16, 64, 256, 1024):
         p = fd.paged_plan(2, 8, 8, "bf16", ps, 1 << 20, 2 << 20, 256)
