@@ -568,3 +568,19 @@ def test_decode_any_finite_scale(H, Hkv, scale, device):
                            max_seq_len=1000, total_kv=1000, opt=fd.options(force_chunk=256))
     torch.cuda.synchronize()
     assert_close(o[0], ref, "bf16", f"paged scale={scale}")
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("H,Hkv", [(64, 4), (64, 2), (48, 3)])
+def test_paged_large_head_groups(H, Hkv, kernel, device):
+    """Paged batches with 16 and 32 query heads per KV head (the matrix-core kernel
+    splits a group over several workgroups) and 16 over an odd KV-head count, on
+    ragged lengths that give one-split and many-split sequences."""
+    lens = [5, 300, 1500, 4000]
+    d = inputs.paged_inputs(len(lens), H, Hkv, 128, "f16", 16, lens, 930 + H + Hkv)
+    announce(f"paged large groups H={H} Hkv={Hkv} {kernel}")
+    o = run_paged(d, device, opt=fd.options(force_chunk=512, kernel=kernel))
+    pairs = [(b, h) for b in range(len(lens)) for h in (0, H // 2 - 1, H // 2, H - 1)]
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"], pairs=pairs)
+    assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, "f16", f"H={H} Hkv={Hkv} {kernel}")
