@@ -584,3 +584,18 @@ def test_paged_large_head_groups(H, Hkv, kernel, device):
     ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
                                            16, d["scale"], pairs=pairs)
     assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, "f16", f"H={H} Hkv={Hkv} {kernel}")
+
+
+def test_paged_long_sequence(device):
+    """A 128k-token sequence beside a 100-token one in a paged GQA4 batch (8192
+    pages of 16 tokens, shuffled): the planner's largest paged strides, table
+    slices staged across many pages, on sampled heads of both sequences."""
+    lens = [131072, 100]
+    d = inputs.paged_inputs(2, 32, 8, 128, "bf16", 16, lens, 940)
+    plan = fd.paged_plan(2, 32, 8, "bf16", 16, max(lens), sum(lens), 0)
+    announce(f"paged long sequence plan chunk={plan['chunk']} splits={plan['num_splits']}")
+    o = run_paged(d, device)
+    pairs = [(b, h) for b in range(2) for h in (0, 13, 31)]
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"], pairs=pairs)
+    assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, "bf16", "paged 128k")
