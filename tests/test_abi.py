@@ -256,3 +256,21 @@ def test_prefill_rejects_bad_arguments_without_a_device():
     assert call(B=65535, H=65535, Hkv=65535, N=64) == 2  # grid beyond 31 bits
     assert lib.fd_status_string(call(opt=ctypes.byref(fd.options(force_chunk=100)))).decode() == "FD_ERR_INVALID_ARG"
     assert call(scale=float("nan")) == 1 and "scale" in lib.fd_last_error().decode()
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """Without the built library the binding raises instead of computing anything,
+    and host tensors are refused outright: the product path has no CPU or oracle
+    fallback."""
+    q = torch.zeros(8, 128)
+    k = torch.zeros(16, 8, 128)
+    with pytest.raises(ValueError, match="device tensor"):
+        fd.fd_decode(q, k, k)
+    with pytest.raises(ValueError, match="device tensor"):
+        fd.fd_prefill(q.reshape(1, 1, 8, 128), q.reshape(1, 1, 8, 128), q.reshape(1, 1, 8, 128))
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libfd.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        fd.decode_plan(8, 8, 512, "f32", 256)
