@@ -75,7 +75,7 @@ int target_wgs_per_cu(fd_dtype dtype, bool mha, long long kv_bytes) {
 constexpr double kWgFixedBytes = 32768.0;
 constexpr double kWgFixedBytesList = 3.0 * kWgFixedBytes;
 constexpr int kPagedSlotsPerCu = 2;  // resident split workgroups per CU (two waves per SIMD)
-constexpr int kMinChunk = 64;
+constexpr int kMinChunk = 16;  // one 16-token block: a short cache still spreads over many workgroups
 constexpr int kMaxChunk = 16384;
 constexpr int kMaxSplits = 4096;
 

@@ -44,7 +44,7 @@ def test_status_strings():
 
 
 def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
-    assert p["chunk"] % 64 == 0 and p["chunk"] >= 64
+    assert p["chunk"] % 16 == 0 and p["chunk"] >= 16  # whole 16-token addressing blocks
     # floor: the last split of a sequence also takes the remainder
     assert p["num_splits"] == max(1, max_len // p["chunk"])
     if p["work_list"]:  # splits that hold tokens, numbered; at most the full grid
