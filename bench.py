@@ -398,7 +398,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library and this benchmark run on one GPU)",
               file=sys.stderr)
         return 2
     import torch
