@@ -48,7 +48,10 @@ def kv_head_of(h: int, H: int, Hkv: int) -> int:
 
 
 def scores(q_row: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
-    """s_t = scale * q . k_t for every key row ([FA] "标准注意力的问题")."""
+    """s_t = scale * q . k_t for every key row ([FA] "标准注意力的问题").
+
+    ``q_row`` is one query [D] (result [L]) or several as columns [D, n]
+    (result [L, n], column j the scores of query j)."""
     return (keys @ q_row) * np.float64(scale)
 
 
@@ -67,34 +70,48 @@ def log_sum_exp(s: np.ndarray) -> float:
 
 
 def weighted_sum(p: np.ndarray, values: np.ndarray) -> np.ndarray:
-    """O = P V for one query row."""
+    """O = P V: one weight row [L] gives [D]; several rows [n, L] give [n, D]."""
     return p @ values
 
 
 def decode_attention(q, k, v, scale: float, heads=None, return_weights: bool = False):
     """Single decode, contiguous KV.
 
-    q [H, D], k and v [S, Hkv, D] (torch or numpy, any float dtype; each KV head
-    used is upcast exactly to float64 on its own, so large caches are never
-    copied whole). Returns ``(o [n, D], lse [n])`` for the selected q heads (all
-    by default), plus the list of weight rows if ``return_weights``.
+    q [H, D], k and v [S, Hkv, D] (torch or numpy, any float dtype). Returns
+    ``(o [n, D], lse [n])`` for the selected q heads (all by default), plus the
+    list of weight rows if ``return_weights``.
+
+    The heads are taken a KV head at a time: that head's keys and values are
+    upcast exactly to float64 once, and the scores of all G query heads of the
+    group are one matrix product (column j = query j); each column is then
+    softmaxed on its own and P V is one more product. A group is always
+    computed whole, whichever of its heads were asked for, so a head's result
+    does not depend on the selection. Large caches are never copied whole.
     """
     H, D = q.shape
     S, Hkv = k.shape[0], k.shape[1]
     heads = list(range(H)) if heads is None else [int(h) for h in heads]
     o = np.zeros((len(heads), D), dtype=np.float64)
     lse = np.full(len(heads), -np.inf, dtype=np.float64)
-    weights = []
+    weights = [np.zeros(0)] * len(heads)
+    groups: dict[int, list[int]] = {}
     for i, h in enumerate(heads):
-        g = kv_head_of(h, H, Hkv)
+        groups.setdefault(kv_head_of(h, H, Hkv), []).append(i)
+    for g, idx in groups.items():
         if S == 0:
-            weights.append(np.zeros(0))
             continue
-        s = scores(_f64(q[h]), _f64(k[:, g, :]), scale)
-        p = softmax_weights(s)
-        o[i] = weighted_sum(p, _f64(v[:, g, :]))
-        lse[i] = log_sum_exp(s)
-        weights.append(p)
+        members = [h for h in range(H) if kv_head_of(h, H, Hkv) == g]
+        keys = _f64(k[:, g, :])
+        values = _f64(v[:, g, :])
+        q_cols = np.stack([_f64(q[h]) for h in members], axis=1)  # [D, G]
+        s = scores(q_cols, keys, scale)                            # [S, G]
+        p = np.stack([softmax_weights(s[:, j]) for j in range(len(members))])  # [G, S]
+        og = weighted_sum(p, values)                               # [G, D]
+        for i in idx:
+            j = members.index(heads[i])
+            o[i] = og[j]
+            lse[i] = log_sum_exp(s[:, j])
+            weights[i] = p[j]
     if return_weights:
         return o, lse, weights
     return o, lse
@@ -142,11 +159,14 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, page_size
     pairs = [(int(b), int(h)) for b, h in pairs]
     o = np.zeros((len(pairs), D))
     lse = np.full(len(pairs), -np.inf)
-    for i, (b, h) in enumerate(pairs):
+    by_seq: dict[int, list[int]] = {}
+    for i, (b, _) in enumerate(pairs):
+        by_seq.setdefault(b, []).append(i)
+    for b, idx in by_seq.items():  # one gather per sequence
         kb = gather_pages(k_cache, table[b], lens[b], page_size)
         vb = gather_pages(v_cache, table[b], lens[b], page_size)
-        oo, ll = decode_attention(q[b], kb, vb, scale, heads=[h])
-        o[i], lse[i] = oo[0], ll[0]
+        oo, ll = decode_attention(q[b], kb, vb, scale, heads=[pairs[i][1] for i in idx])
+        o[idx], lse[idx] = oo, ll
     return o, lse
 
 
@@ -178,7 +198,12 @@ def split_partials(q, k, v, scale: float, chunk: int, heads=None, bounds=None):
 
 def paged_split_partials(q, k_cache, v_cache, block_table, seq_lens, page_size: int, scale: float,
                          chunk: int, b: int, h: int, bounds=None):
-    """Split partials of one (sequence b, q head h) of a paged batch: ``(O_s [n, D], lse_s [n])``."""
+    """Split partials of one (sequence b, q head h) of a paged batch: ``(O_s [n, D], lse_s [n])``.
+
+    The sequence's L_b tokens are gathered in logical order through its block
+    table ([FA] "PagedAttention"), then cut as ``split_partials`` cuts a
+    contiguous cache: ``split_bounds(L_b, chunk)``, or the given ``bounds``.
+    """
     table, lens = _ints(block_table), _ints(seq_lens)
     kb = gather_pages(k_cache, table[b], lens[b], page_size)
     vb = gather_pages(v_cache, table[b], lens[b], page_size)

@@ -74,11 +74,11 @@ def paged_decode_attention_e4m3(q, k_cache, v_cache, block_table, seq_lens, page
     pairs = [(int(b), int(h)) for b, h in pairs]
     o = np.zeros((len(pairs), D))
     lse = np.full(len(pairs), -np.inf)
-    cache = {}
-    for i, (b, h) in enumerate(pairs):
-        if b not in cache:
-            cache = {b: rows(b)}
-        kv, vv = cache[b]
-        oo, ll = decode_attention(q[b], kv, vv, scale, heads=[h])
-        o[i], lse[i] = oo[0], ll[0]
+    by_seq: dict[int, list[int]] = {}
+    for i, (b, _) in enumerate(pairs):
+        by_seq.setdefault(b, []).append(i)
+    for b, idx in by_seq.items():  # one gather and dequantisation per sequence
+        kv, vv = rows(b)
+        oo, ll = decode_attention(q[b], kv, vv, scale, heads=[pairs[i][1] for i in idx])
+        o[idx], lse[idx] = oo, ll
     return o, lse

@@ -283,6 +283,32 @@ def pin_paged_equals_contiguous() -> bool:
     return bool(ok)
 
 
+def pin_paged_split_partials() -> bool:
+    """Split partials of a paged sequence equal the contiguous split partials of the same
+    tokens (pinned by pin_split_invariance) for the pages' cut and for the library's
+    (max(1, L // chunk) splits, the last one taking the remainder). The pool is built by
+    hand with NaN in every unused slot and page, so a wrong page, slot, sequence or
+    length shows. The split lse values combine (scipy logsumexp) to the lse of the whole
+    sequence, and merge_lse of the partials gives the paged result."""
+    lens = [1, 17, 1000, 4096]
+    q, ks, vs, kc, vc, table, L = _paged_case(lens)
+    o_full, lse_full = oracle.paged_decode_attention(q, kc, vc, table, L, 16, 0.25)
+    ok = True
+    for b, h, chunk, library_cut in ((0, 0, 16, False), (1, 7, 16, True), (2, 9, 64, False), (2, 30, 64, True),
+                                     (3, 31, 1024, True), (3, 4, 100, False), (3, 12, 4096, True)):
+        n = max(1, lens[b] // chunk)
+        bounds = ([(s * chunk, lens[b] if s == n - 1 else (s + 1) * chunk) for s in range(n)]
+                  if library_cut else None)
+        O_s, lse_s = oracle.paged_split_partials(q, kc, vc, table, L, 16, 0.25, chunk, b, h, bounds=bounds)
+        Oc, lc = oracle.split_partials(q[b], ks[b], vs[b], 0.25, chunk, heads=[h], bounds=bounds)
+        ok &= O_s.shape == Oc[0].shape and np.array_equal(O_s, Oc[0]) and np.array_equal(lse_s, lc[0])
+        ok &= bool(np.isfinite(O_s).all()) and O_s.shape[0] == (n if library_cut else -(-lens[b] // chunk))
+        ok &= abs(scipy.special.logsumexp(lse_s) - lse_full[b, h]) < 1e-11
+        o, _ = oracle.merge_lse(O_s, lse_s)
+        ok &= np.allclose(o, o_full[b, h], rtol=1e-12, atol=1e-13)
+    return bool(ok)
+
+
 def pin_e4m3_decoding() -> bool:
     """Every E4M3 code against torch's float8_e4m3fn decoding (a library routine), plus
     the format's landmarks: 1.0, the largest finite 448, the smallest subnormal 2^-9."""
@@ -367,7 +393,7 @@ def pin_prefill_rows_are_decodes() -> bool:
 PINS = [pin_worked_example, pin_two_keys_logistic, pin_rows_sum_to_one, pin_identical_keys_mean,
         pin_zero_scale_mean, pin_single_key_exact, pin_lse_scipy, pin_torch_sdpa, pin_gqa_mapping,
         pin_brute_force_recurrences, pin_split_invariance, pin_merge_forms_agree,
-        pin_paged_equals_contiguous, pin_e4m3_decoding, pin_e4m3_attention, pin_prefill_torch_sdpa,
+        pin_paged_equals_contiguous, pin_paged_split_partials, pin_e4m3_decoding, pin_e4m3_attention, pin_prefill_torch_sdpa,
         pin_prefill_rows_are_decodes]
 
 
@@ -412,6 +438,9 @@ MUTANTS = {
                                lambda L, chunk: [(s, s + chunk) for s in range(0, (L // chunk) * chunk, chunk)]),
     "merge_ignores_lse": ("merge_lse", lambda O_s, lse_s: (np.asarray(O_s).mean(axis=0), float(np.max(lse_s)))),
     "page_slot_swapped": ("gather_pages", None),
+    "paged_partials_ignore_bounds": ("paged_split_partials", lambda *a, bounds=None: _bad_partials(*a, cut="pages")),
+    "paged_partials_drop_last_token": ("paged_split_partials", lambda *a, bounds=None: _bad_partials(*a, bounds=bounds,
+                                                                                                    short=1)),
     "e4m3_bias_8": ("E4M3_TABLE", None),
     "e4m3_scales_swapped": ("decode_attention_e4m3", None),
     "causal_off_by_one": ("causal_mask", lambda n_q, n_k: np.arange(n_k)[None, :] < np.arange(n_q)[:, None]),
@@ -424,6 +453,17 @@ def _bad_gather(cache, table_row, L, page_size):
     table_row = np.asarray(table_row, dtype=np.int64)
     t = np.arange(int(L))
     return np.asarray(cache)[table_row[t // page_size], (page_size - 1) - t % page_size]
+
+
+def _bad_partials(q, k_cache, v_cache, block_table, seq_lens, page_size, scale, chunk, b, h, bounds=None,
+                  cut="given", short=0):
+    """paged_split_partials with a planted mistake: the given token ranges ignored (the
+    pages' cut used instead), or a sequence gathered one token short."""
+    table, lens = od._ints(block_table), od._ints(seq_lens)
+    kb = od.gather_pages(k_cache, table[b], lens[b] - short, page_size)
+    vb = od.gather_pages(v_cache, table[b], lens[b] - short, page_size)
+    O_s, lse_s = od.split_partials(q[b], kb, vb, scale, chunk, heads=[h], bounds=None if cut == "pages" else bounds)
+    return O_s[0], lse_s[0]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
