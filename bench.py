@@ -42,20 +42,23 @@ def log(msg: str) -> None:
     sys.stderr.flush()
 
 
-# The sources each timed kernel is built from (a counter profile is tied to them).
+# The sources each timed kernel and its launch are built from (a counter profile is
+# tied to them): the kernel, the shared device code and, for the planner that sets
+# the grid and the split stride, the C-ABI layer and its header.
+_CSRC = "decode_attention_13_amd/csrc/"
+_COMMON = (_CSRC + "fd_device.h", _CSRC + "fd_internal.h", _CSRC + "fd_api.hip", "include/fd.h")
 KERNEL_SOURCES = {
-    "split_valu_kernel": ("fd_split_valu.hip", "fd_device.h", "fd_internal.h"),
-    "split_mfma_kernel": ("fd_split_mfma.hip", "fd_device.h", "fd_internal.h"),
-    "prefill_kernel": ("fd_prefill.hip", "fd_device.h", "fd_internal.h"),
+    "split_valu_kernel": (_CSRC + "fd_split_valu.hip",) + _COMMON,
+    "split_mfma_kernel": (_CSRC + "fd_split_mfma.hip",) + _COMMON,
+    "prefill_kernel": (_CSRC + "fd_prefill.hip",) + _COMMON,
 }
 
 
 def kernel_source_hash(kernel: str) -> str:
     """Hash of one kernel's HIP sources: a committed counter profile is used only while it matches."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_attention_13_amd", "csrc")
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -75,7 +78,8 @@ def load_traffic(kernel: str, workload: str) -> dict | None:
 class Case:
     """A workload placed in device memory with rotated KV copies and its C-ABI arguments."""
 
-    def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None, kv: str = "native"):
+    def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None, kv: str = "native",
+                 merge: str = "auto"):
         import torch
 
         import decode_attention_13_amd as fd
@@ -94,7 +98,8 @@ class Case:
             data = with_fp8_kv(data)
         d = data
         self.d = d
-        self.opt = fd.options(force_chunk=chunk, kernel=kernel) if (chunk or kernel != "auto") else None
+        forced = chunk or kernel != "auto" or merge != "auto"
+        self.opt = fd.options(force_chunk=chunk, kernel=kernel, merge=merge) if forced else None
         qdt = inputs_dtype(w.dtype)
         esize = 1 if self.fp8 else torch.tensor([], dtype=qdt).element_size()
         self.dtype_code = binding.FD_DTYPE_KV_E4M3[qdt] if self.fp8 else binding.FD_DTYPE[qdt]
@@ -184,6 +189,7 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
     opts = [case.fd.options(force_num_splits=base.force_num_splits if base else 0,
                             force_chunk=base.force_chunk if base else 0,
                             kernel=base.force_kernel if base else 0,
+                            merge=base.force_merge if base else 0,
                             split_begin_event=begins[i], split_end_event=ends[i]) for i in range(steps)]
     torch.cuda.synchronize()
     for i in range(warmup):  # back to steady state after the synchronisations
@@ -198,32 +204,81 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and stepping."""
+    info = {}
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block
+                k, _, v = line.partition(":")
+                info[k.strip()] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({ids})" if ids else name
+
+
+def host_cores() -> int:
+    """Cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _oracle_step_single(d, fp8: bool) -> float:
+    """Wall time of one whole oracle decode step (every head) of a contiguous workload."""
+    import oracle
+    t0 = time.perf_counter()
+    if fp8:
+        oracle.decode_attention_e4m3(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["scale"])
+    else:
+        oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    return time.perf_counter() - t0
 
 
 def cpu_baseline(w, budget_s: float = 12.0, fp8: bool = False) -> dict:
-    """The float64 oracle as it stands, timed on this host over a bounded sample
-    (the E4M3 form of the oracle when the cache is FP8)."""
+    """The float64 oracle as it stands, timed on this host with its BLAS threads set
+    to the cores of this process (the E4M3 form of the oracle when the cache is FP8).
+
+    Workloads whose whole step takes under a few seconds (the 512-token fp32 and the
+    4k bf16 decodes) are timed as whole steps, median of 3 after one untimed run;
+    larger ones over a bounded sample of heads or sequences. The 512-token fp32
+    decode is also timed on one thread."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from decode_attention_13_amd.inputs import WORKLOADS
+    threads = host_cores()
+    with threadpool_limits(limits=threads):
+        out = _cpu_baseline(w, budget_s, fp8, np, oracle)
+    small = WORKLOADS["decode_f32_h8_s512"]
+    ds = small.make()
+    _oracle_step_single(ds, False)
+    with threadpool_limits(limits=1):
+        one = sorted(_oracle_step_single(ds, False) for _ in range(3))[1]
+    out.update({"cores": threads, "cpu": cpu_model(),
+                "single_thread": {"workload": small.name, "us_per_step": round(one * 1e6, 1),
+                                  "value": round(small.kv_bytes() / one / 1e9, 4), "unit": "GB/s", "cores": 1}})
+    return out
+
+
+def _cpu_baseline(w, budget_s, fp8, np, oracle) -> dict:
     d = w.make()
     if fp8:
         from decode_attention_13_amd.inputs import with_fp8_kv
         d = with_fp8_kv(d)
+    kv_bytes = 2 * _kv_elems(w, d) if fp8 else w.kv_bytes()  # E4M3: one byte per element
+    if w.kind == "single" and w.S * w.H <= 4096 * 32:
+        _oracle_step_single(d, fp8)
+        runs = sorted(_oracle_step_single(d, fp8) for _ in range(3))
+        step_s = runs[1]
+        return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                "sample": f"whole steps of {w.name}, median of 3 ({', '.join(f'{r * 1e3:.1f}' for r in runs)} ms)",
+                "us_per_step": round(step_s * 1e6, 1)}
     if w.kind == "single":
         heads = list(range(w.H))
         n_done = 0
@@ -259,8 +314,7 @@ def cpu_baseline(w, budget_s: float = 12.0, fp8: bool = False) -> dict:
         el = time.perf_counter() - t0
         sample = f"{n_done} whole sequences (all {w.H} heads) of {w.name}, {el:.1f} s"
         step_s = el / tokens_done * float(lens.sum())
-    kv_bytes = 2 * _kv_elems(w, d) if fp8 else w.kv_bytes()  # E4M3: one byte per element
-    return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads, "cpu": cpu_model(), "kind": "oracle",
+    return {"value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "kind": "oracle",
             "sample": sample, "us_per_step": round(step_s * 1e6, 1)}
 
 
@@ -350,12 +404,15 @@ def bench_prefill(args) -> dict:
 
 def cpu_baseline_prefill(w, d, budget_s: float = 12.0) -> dict:
     """The float64 oracle's prefill, one (sequence, head) at a time, over a bounded sample."""
+    from threadpoolctl import threadpool_limits
+
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = host_cores()
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline_prefill(w, d, budget_s, threads, oracle)
+
+
+def _cpu_baseline_prefill(w, d, budget_s, threads, oracle) -> dict:
     n_done = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
@@ -388,6 +445,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--chunk", type=int, default=0, help="force tokens per split (multiple of 64)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"], help="force the split kernel")
+    ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "fused"],
+                    help="force how split partials are merged (merge kernel, or the last workgroups)")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="cache storage: the workload's dtype, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--sweep", action="store_true",
@@ -415,7 +474,7 @@ def main() -> int:
         print(json.dumps(bench_prefill(args)), flush=True)
         return 0
     w = WORKLOADS[args.workload]
-    case = Case(w, args.chunk, args.kernel, kv=args.kv)
+    case = Case(w, args.chunk, args.kernel, kv=args.kv, merge=args.merge)
     split_kernel = SPLIT_KERNELS[case.plan["kernel"]]
     wl_name = w.name + ("_kv_e4m3" if case.fp8 else "")
     t = time_steps(case, args.steps, args.warmup)

@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     FdError,
     FdOptions,
     decode_plan,
+    decode_workspace_size,
     device_num_cus,
     fd_decode,
     fd_decode_fp8kv,
@@ -18,5 +19,6 @@ from .binding import (  # noqa: F401
     new_workspace,
     options,
     paged_plan,
+    paged_workspace_size,
     workspace_views,
 )

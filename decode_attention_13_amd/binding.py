@@ -24,14 +24,16 @@ FD_DTYPE_KV_E4M3 = {torch.float16: 3, torch.bfloat16: 4}
 FP8_CODES = {"f16_kv_e4m3": 3, "bf16_kv_e4m3": 4}
 FP8_CACHE_DTYPES = (torch.float8_e4m3fn, torch.uint8)  # uint8 = raw E4M3 codes
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+MERGES = {"auto": 0, "kernel": 1, "fused": 2}
+WS_COUNTER_BYTES = 16384  # zeroed head block of every workspace (include/fd.h)
 HEAD_DIM = 128
 CHUNK_QUANTUM = 64
 
 
 class FdOptions(ctypes.Structure):
     _fields_ = [("force_num_splits", ctypes.c_int), ("force_chunk", ctypes.c_int), ("force_kernel", ctypes.c_int),
-                ("reserved", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
-                ("split_end_event", ctypes.c_void_p)]
+                ("debug_checks", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
+                ("split_end_event", ctypes.c_void_p), ("force_merge", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
 class FdPlan(ctypes.Structure):
@@ -39,7 +41,8 @@ class FdPlan(ctypes.Structure):
                 ("num_splits", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("grid_z", ctypes.c_int), ("threads", ctypes.c_int), ("merge", ctypes.c_int),
                 ("kv_heads_per_group", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
-                ("ws_lse_offset", ctypes.c_size_t), ("work_list", ctypes.c_int), ("reserved2", ctypes.c_int)]
+                ("ws_lse_offset", ctypes.c_size_t), ("work_list", ctypes.c_int), ("reserved2", ctypes.c_int),
+                ("ws_err_offset", ctypes.c_size_t), ("ws_o_offset", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved2"}
@@ -85,6 +88,12 @@ SIGNATURES = {
     "fd_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                   ctypes.c_int, ctypes.POINTER(FdOptions), ctypes.c_void_p]),
+    "fd_decode_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.POINTER(FdOptions),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "fd_paged_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                                               ctypes.POINTER(FdOptions), ctypes.POINTER(ctypes.c_size_t)]),
     "fd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fd_last_error": (ctypes.c_char_p, []),
 }
@@ -112,15 +121,20 @@ def _check(status: int) -> None:
 
 
 def options(force_num_splits: int = 0, force_chunk: int = 0, kernel: str | int = "auto",
-            split_begin_event=None, split_end_event=None) -> FdOptions:
-    """An ``fd_options`` block; events are ``torch.cuda.Event`` objects (or raw handles)."""
+            split_begin_event=None, split_end_event=None, debug_checks: bool | int = False,
+            merge: str | int = "auto") -> FdOptions:
+    """An ``fd_options`` block; events are ``torch.cuda.Event`` objects (or raw handles).
+    ``debug_checks``: paged calls check the block table and lengths on the device and
+    raise ``FdError`` (FD_ERR_BAD_DATA) on an out-of-range value (the call synchronises).
+    ``merge``: "kernel" (a merge kernel), "fused" (the last workgroups merge) or "auto"."""
     def handle(ev):
         if ev is None:
             return None
         return ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return FdOptions(int(force_num_splits), int(force_chunk), k, 0, handle(split_begin_event),
-                     handle(split_end_event))
+    mg = MERGES[merge] if isinstance(merge, str) else int(merge)
+    return FdOptions(int(force_num_splits), int(force_chunk), k, int(debug_checks), handle(split_begin_event),
+                     handle(split_end_event), mg, 0)
 
 
 def _opt_ptr(opt):
@@ -164,6 +178,21 @@ def paged_plan(B: int, H: int, Hkv: int, dtype, page_size: int, max_seq_len: int
     return p.as_dict()
 
 
+def decode_workspace_size(H: int, Hkv: int, S: int, dtype, num_cus: int = 0, opt: FdOptions | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().fd_decode_workspace_size(H, Hkv, S, HEAD_DIM, _dtype_code(dtype), num_cus, _opt_ptr(opt),
+                                          ctypes.byref(n)))
+    return int(n.value)
+
+
+def paged_workspace_size(B: int, H: int, Hkv: int, dtype, page_size: int, max_seq_len: int, total_kv: int = 0,
+                         num_cus: int = 0, opt: FdOptions | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().fd_paged_workspace_size(B, H, Hkv, HEAD_DIM, _dtype_code(dtype), page_size, max_seq_len, total_kv,
+                                         num_cus, _opt_ptr(opt), ctypes.byref(n)))
+    return int(n.value)
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -180,8 +209,9 @@ def _require(t: torch.Tensor, name: str, dtype=None) -> None:
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """An uninitialised workspace of ``nbytes`` (uint8); it needs no initialisation."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A workspace of ``nbytes`` (uint8) whose counter block is zero, as every call
+    needs it on first use (the rest is never read before it is written)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def _workspace(ws, need: int, device) -> tuple[int, int, torch.Tensor | None]:
@@ -342,7 +372,8 @@ def workspace_views(ws: torch.Tensor, plan: dict, B: int, H: int) -> tuple[torch
     """(ws_o [B, H, num_splits, D], ws_lse [B, H, num_splits]) float32 views of a workspace."""
     n = plan["num_splits"]
     rows = B * H * n
-    o = ws[: rows * HEAD_DIM * 4].view(torch.float32).view(B, H, n, HEAD_DIM)
+    o0 = plan["ws_o_offset"]
+    o = ws[o0: o0 + rows * HEAD_DIM * 4].view(torch.float32).view(B, H, n, HEAD_DIM)
     off = plan["ws_lse_offset"]
     lse = ws[off: off + rows * 4].view(torch.float32).view(B, H, n)
     return o, lse

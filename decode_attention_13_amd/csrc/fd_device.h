@@ -419,6 +419,37 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
     }
 }
 
+// ---------------------------------------------------------------- debug checks
+// With fd_options.debug_checks a paged split records the first out-of-range
+// value it meets (the kernels clamp either way, so no access leaves the cache):
+// the workgroup of a sequence's last split checks L_b against [0, max_len],
+// and every split checks the table entries of the blocks it reads. The
+// winner of the compare-and-swap on the kind word writes the rest.
+__device__ __forceinline__ void report_bad(int *err, int kind, int b, int index, int value) {
+    if (atomicCAS(err, 0, kind) == 0) {
+        err[1] = b;
+        err[2] = index;
+        err[3] = value;
+    }
+}
+
+// Every thread of the workgroup calls this (no barrier inside). The split reads
+// tokens [t_begin, t_end) (t_end <= t_begin when the split is empty); not_last
+// is 0 for the workgroup that owns the sequence's last split.
+__device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int t_begin, int t_end, int not_last) {
+    if (!not_last && threadIdx.x == 0) {
+        const int L_raw = a.seq_lens[b];
+        if (L_raw < 0 || L_raw > a.max_len) report_bad(a.err, kBadSeqLen, b, 0, L_raw);
+    }
+    if (t_end <= t_begin) return;
+    const int first = t_begin >> a.page_shift, last = (t_end - 1) >> a.page_shift;
+    const int32_t *row = a.block_table + (size_t)b * a.max_blocks;
+    for (int i = first + (int)threadIdx.x; i <= last; i += kSplitThreads) {
+        const int page = row[i];
+        if (page < 0 || page >= a.num_pages) report_bad(a.err, kBadTableEntry, b, i, page);
+    }
+}
+
 // ---------------------------------------------------------------- split boundaries
 // A sequence of L tokens has max(1, floor(L / chunk)) splits (none if L = 0):
 // split s covers [s*chunk, (s+1)*chunk) except the last, which runs to L and so
@@ -561,11 +592,107 @@ __device__ __forceinline__ bool paged_item(const SplitArgs &a, int *s_start, int
 }
 
 // ---------------------------------------------------------------- split epilogue
+// Partials read by another workgroup of the same launch (fused merge) are
+// written and read as device-scope relaxed atomics: on gfx950 these are plain
+// vector stores and loads with the sc1 bit, which write through and read past
+// the per-XCD L2 caches, so they are coherent across the chip without an L2
+// writeback.
+__device__ __forceinline__ void store_device(float *p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// End of a split in a fused launch ("[CUDA 优化实战] 纯手搓 flash decoding sm120",
+// section "1. flash decoding": the partials of a (sequence, head) are combined
+// once all of its splits are done; here the last of its workgroups does it
+// instead of a second kernel). Every wave first waits until its partial stores
+// have completed, then one thread counts the workgroup in on the (sequence,
+// head slice) counter; the workgroup that brings it to n_b resets it to zero
+// for the next call and merges the n_b partials of its nh heads by log-sum-exp
+// (the merge kernel's arithmetic): w_s = e^(lse_s - max lse) / sum_s' e^(...),
+// o = sum_s w_s O_s. No thread waits for another workgroup, so nothing can
+// hang: the last one to arrive always finds every partial in place.
+// The merging thread of output element (h, d) loads every lse_s of head h and
+// every O_s[d] before it uses any, so the merge costs one round trip to memory
+// (each of these loads crosses the L2 to reach the other XCDs' stores); the
+// planner fuses only where nh * n_b is at most kFusedMaxRows (at most nh * n_b /
+// 2 + n_b loads per thread).
+template <typename T, int NS>
+__device__ __forceinline__ void fused_merge_rows(const SplitArgs &a, int b, int h0, int nh, int n_b) {
+    const size_t row0 = ((size_t)b * a.H + h0) * a.num_splits;
+    // elements per thread and pass: 32 partial values (and as many lse values) in registers
+    constexpr int kPer = (32 / NS) < 8 ? (32 / NS) : 8;
+    for (int i0 = 0; i0 < nh * kHeadDim; i0 += kSplitThreads * kPer) {
+        float lse[kPer][NS], x[kPer][NS];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int i = min(i0 + e * kSplitThreads + (int)threadIdx.x, nh * kHeadDim - 1);
+            const int hh = i / kHeadDim;
+            const int d = i - hh * kHeadDim;
+            const float *lrow = a.ws_lse + row0 + (size_t)hh * a.num_splits;
+            const float *orow = a.ws_o + (row0 + (size_t)hh * a.num_splits) * kHeadDim + d;
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp) {
+                const int s2 = min(sp, n_b - 1);
+                lse[e][sp] = load_device(lrow + s2);
+                x[e][sp] = load_device(orow + (size_t)s2 * kHeadDim);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int i = i0 + e * kSplitThreads + (int)threadIdx.x;
+            if (i >= nh * kHeadDim) break;
+            const int hh = i / kHeadDim;
+            const int d = i - hh * kHeadDim;
+            float M = -INFINITY;
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp)
+                if (sp < n_b) M = fmaxf(M, lse[e][sp]);
+            const float mu = finite_or_zero(M);
+            float W = 0.f, o = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp) {
+                if (sp < n_b) {
+                    const float w = exp2_fast((lse[e][sp] - mu) * kLog2e);
+                    W += w;
+                    o = __builtin_fmaf(w, x[e][sp], o);
+                }
+            }
+            reinterpret_cast<T *>(a.out)[((size_t)b * a.H + h0 + hh) * kHeadDim + d] =
+                Elem<T>::store_cast(W > 0.f ? o / W : 0.f);
+        }
+    }
+}
+
+template <typename T>
+__device__ void fused_merge_tail(const SplitArgs &a, int b, int h0, int nh, int n_b) {
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's partial stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned *ctr = a.counters + (size_t)b * gridDim.x + blockIdx.x;
+        const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev + 1u == (unsigned)n_b;
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;  // uniform over the workgroup
+    // n_b rounded up to a compiled split count (at most kFusedMaxSplits)
+    if (n_b <= 4) fused_merge_rows<T, 4>(a, b, h0, nh, n_b);
+    else if (n_b <= 8) fused_merge_rows<T, 8>(a, b, h0, nh, n_b);
+    else if (n_b <= 16) fused_merge_rows<T, 16>(a, b, h0, nh, n_b);
+    else fused_merge_rows<T, 32>(a, b, h0, nh, n_b);
+}
+
 // Stores one workgroup's result for query heads h0 .. h0+nh-1 of sequence b,
 // split `split` of n_b. value(hh, d, lse) returns the split's normalised
 // output element and sets its natural-log lse. When n_b == 1 the split is the
 // whole sequence and o is written directly; otherwise the partial goes to the
-// workspace for the merge kernel.
+// workspace, for the merge kernel or (fused launch) for the last workgroup of
+// the sequence's head slice.
 template <typename T, typename ValueFn>
 __device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int split, int n_b, ValueFn value) {
     const bool direct = n_b == 1;
@@ -577,12 +704,17 @@ __device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int spli
         const size_t bh = (size_t)b * a.H + h0 + hh;
         if (direct) {
             reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = Elem<T>::store_cast(o);
+        } else if (a.fused) {
+            const size_t row = bh * a.num_splits + split;
+            store_device(a.ws_o + row * kHeadDim + d, o);
+            if (d == 0) store_device(a.ws_lse + row, lse);
         } else {
             const size_t row = bh * a.num_splits + split;
             a.ws_o[row * kHeadDim + d] = o;
             if (d == 0) a.ws_lse[row] = lse;
         }
     }
+    if (!direct && a.fused) fused_merge_tail<T>(a, b, h0, nh, n_b);
 }
 
 }  // namespace fd

@@ -43,7 +43,20 @@ struct SplitArgs {
     int B;                  // sequences (paged)
     int work_list;          // 1: grid y numbers the splits that hold tokens (paged; see the split kernels)
     int grid_items;         // grid y when work_list is set
+    int *err;               // paged with debug_checks: 4-int error record (kind, sequence, index, value); else NULL
+    unsigned *counters;     // fused launch: one counter per (sequence, head slice), zero between calls
+    int fused;              // 1: the last workgroup of each (sequence, head slice) merges (no merge kernel)
 };
+
+// Fused launches: splits per sequence and heads per workgroup one workgroup
+// merges at the end, and counters at the head of every workspace.
+constexpr int kFusedMaxSplits = 32;
+constexpr int kFusedMaxHeads = 16;
+constexpr int kFusedMaxRows = 64;  // heads x splits one workgroup merges (4 x 32 or 16 x 4, ...)
+constexpr int kWsCounters = FD_WS_COUNTER_BYTES / 4;
+
+// Kinds of the debug error record.
+enum BadData { kBadTableEntry = 1, kBadSeqLen = 2 };
 
 // Sequences a work-list launch can hold (its per-sequence offsets live in LDS).
 constexpr int kMaxListSeqs = 1024;

@@ -173,6 +173,10 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
     int page_first = 0;
     const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
     const int n_b = splits_of(L, a.chunk);
+    if constexpr (PAGED) {
+        if (a.err != nullptr)
+            check_paged_split(a, b, t_begin, split < n_b ? split_end(split, n_b, L, a.chunk) : t_begin, not_last);
+    }
     if (split >= n_b - not_last) {  // uniform over the workgroup
         if (split == 0 && !not_last) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;

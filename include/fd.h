@@ -45,6 +45,7 @@ extern "C" {
 
 #define FD_HEAD_DIM 128
 #define FD_CHUNK_QUANTUM 64 /* a forced chunk must be a positive multiple of this */
+#define FD_WS_COUNTER_BYTES 16384 /* counter block at the head of every workspace (see the layout below) */
 
 typedef enum fd_dtype {
     FD_DTYPE_F32 = 0,
@@ -63,8 +64,16 @@ typedef enum fd_status {
     FD_ERR_UNSUPPORTED = 2, /* D != 128, page_size not a power of two in [1, 1024], dtype not valid for the call */
     FD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than fd_plan.workspace_bytes */
     FD_ERR_DEVICE = 4,      /* no current HIP device / attribute query failed */
-    FD_ERR_LAUNCH = 5       /* a kernel launch or event record returned an error */
+    FD_ERR_LAUNCH = 5,      /* a kernel launch or event record returned an error */
+    FD_ERR_BAD_DATA = 6     /* debug_checks only: a block-table entry or sequence length that the
+                               kernels read on the device was out of range (see fd_options) */
 } fd_status;
+
+enum {
+    FD_MERGE_AUTO = 0,   /* planner's choice */
+    FD_MERGE_KERNEL = 1, /* a second kernel merges the split partials */
+    FD_MERGE_FUSED = 2   /* the last workgroup of each (sequence, head slice) merges them: one launch */
+};
 
 enum {
     FD_KERNEL_AUTO = 0, /* planner's choice */
@@ -79,10 +88,24 @@ typedef struct fd_options {
                              multiple of FD_CHUNK_QUANTUM not above max_len / n, at least the quantum) */
     int force_chunk;      /* > 0: the split stride, a multiple of FD_CHUNK_QUANTUM (wins over force_num_splits) */
     int force_kernel;     /* FD_KERNEL_* */
-    int reserved;         /* must be 0 */
+    int debug_checks;     /* 0 or 1. Paged calls with 1: the split kernels check every block-table
+                             entry they address ([0, num_pages)) and every sequence length
+                             ([0, min(max_seq_len, max_blocks * page_size)]) and record the first
+                             violation in the workspace (fd_plan.ws_err_offset). They still clamp,
+                             so no access leaves the cache. The call then waits for its kernels
+                             (it synchronises `stream`; not for graph capture) and returns
+                             FD_ERR_BAD_DATA, naming the sequence, table index and value, if any
+                             check failed. Contiguous calls have no device-side index to check and
+                             ignore it. The tables the pages' paged kernel reads are padded with -1
+                             past each sequence's pages ("FlashAttention 与推理算子", section
+                             "一个分页 decode attention kernel（支持 GQA）"): entries past
+                             ceil(L_b / page_size) are never read and never reported. */
     void *split_begin_event; /* hipEvent_t stamped when the split kernel starts executing, or NULL */
     void *split_end_event;   /* hipEvent_t stamped when the split kernel finishes, or NULL
                                 (both set by the dispatch itself: hipExtLaunchKernel) */
+    int force_merge;         /* FD_MERGE_*: how the partials of a multi-split plan are merged;
+                                FD_MERGE_FUSED where the plan cannot fuse is FD_ERR_UNSUPPORTED */
+    int reserved;            /* must be 0 */
 } fd_options;
 
 /* What a call with the same arguments would launch. */
@@ -94,30 +117,47 @@ typedef struct fd_plan {
     int grid_x, grid_y, grid_z; /* split kernel grid: (head slices = Hkv / kv_heads_per_group *
                                    (H / Hkv) / heads_per_group, splits, sequences); see work_list */
     int threads;         /* split kernel workgroup size */
-    int merge;           /* 1: partials go to the workspace and a merge kernel runs; 0: o written directly */
+    int merge;           /* 0: one split per sequence, o written directly; 1 (FD_MERGE_KERNEL): partials
+                            go to the workspace and a merge kernel runs; 2 (FD_MERGE_FUSED): one launch, the
+                            last workgroup of each (sequence, head slice) merges its partials */
     int kv_heads_per_group; /* adjacent KV heads one workgroup reads together (vector-ALU kernel with
                                H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
-    size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0) */
+    size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0 and no debug record) */
     size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
     int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens (the last
                                split of every sequence first, then the others sequence by sequence),
                                grid_z = 1, one split per workgroup; chosen when the (splits x
                                sequences) grid would be mostly empty splits and total_kv is known */
     int reserved2;
+    size_t ws_err_offset;   /* paged plans with debug_checks: byte offset of the 16-byte error
+                               record (int32 kind, sequence, table index or 0, offending value;
+                               kind 1 = table entry, 2 = sequence length) inside the workspace,
+                               which workspace_bytes then includes; 0 otherwise */
+    size_t ws_o_offset;     /* byte offset of ws_o inside the workspace (FD_WS_COUNTER_BYTES) */
 } fd_plan;
 
 /*
- * Workspace layout when merge == 1 (fp32, row-major, from byte 0; no
- * initialisation needed):
- *   ws_o  [B, H, num_splits, D]  normalised output of each split
- *   ws_lse[B, H, num_splits]     natural-log log-sum-exp of each split's scores,
- *                                at byte offset ws_lse_offset.
+ * Workspace layout when merge != 0 (every plan uses the same head block, so one
+ * workspace serves calls of any plan):
+ *   counters [FD_WS_COUNTER_BYTES / 4] uint32 at byte 0: a fused launch counts
+ *                                the finished splits of each (sequence, head
+ *                                slice) here. They must be ZERO before the
+ *                                workspace is first used (e.g. hipMemset once
+ *                                after allocating it); every completed call
+ *                                leaves them zero.
+ *   ws_o  [B, H, num_splits, D]  fp32, normalised output of each split, at
+ *                                byte offset ws_o_offset
+ *   ws_lse[B, H, num_splits]     fp32, natural-log log-sum-exp of each split's
+ *                                scores, at byte offset ws_lse_offset.
+ * ws_o and ws_lse need no initialisation; the debug record, when asked for,
+ * follows at ws_err_offset and is cleared by the call itself.
  * Sequence b has n_b = max(1, floor(L_b / chunk)) splits (none when L_b = 0).
  * Split s < n_b - 1 covers tokens [s*chunk, (s+1)*chunk); the last split covers
  * [(n_b - 1)*chunk, L_b), i.e. chunk to 2*chunk - 1 tokens (fewer only when it is
  * the only split), so no split is a short remainder. Only the splits of
  * sequences with n_b > 1 are written; a sequence with one split is written to
- * o directly. The pages cut a sequence into ceil(L_b / chunk) splits with a
+ * o directly (and in a fused launch the last split's workgroup merges). The
+ * pages cut a sequence into ceil(L_b / chunk) splits with a
  * short last one; folding the remainder into the last full split gives the
  * same result up to rounding and spares a workgroup that would read few
  * tokens for a full workgroup's fixed cost. The split
@@ -140,6 +180,20 @@ fd_status fd_decode_plan(int H, int Hkv, int S, int D, fd_dtype dtype, int num_c
 fd_status fd_paged_plan(int B, int H, int Hkv, int D, fd_dtype dtype, int page_size,
                         int max_seq_len, long long total_kv, int num_cus,
                         const fd_options *opt, fd_plan *out);
+
+/*
+ * Workspace bytes a call with these arguments needs (fd_plan.workspace_bytes of
+ * the matching plan; 0 when every sequence fits one split and no debug record is
+ * asked for). The split planner of "[CUDA 优化实战] 纯手搓 flash decoding sm120",
+ * section "1. flash decoding" sizes the per-split output and log-sum-exp buffers
+ * the same way: one row of D + 1 floats per (sequence, head, split). num_cus as
+ * in the plan calls. *bytes is written only on FD_OK.
+ */
+fd_status fd_decode_workspace_size(int H, int Hkv, int S, int D, fd_dtype dtype, int num_cus,
+                                   const fd_options *opt, size_t *bytes);
+fd_status fd_paged_workspace_size(int B, int H, int Hkv, int D, fd_dtype dtype, int page_size,
+                                  int max_seq_len, long long total_kv, int num_cus,
+                                  const fd_options *opt, size_t *bytes);
 
 /*
  * Single decode over a contiguous KV cache ("[CUDA 优化实战] 纯手搓 flash
@@ -172,7 +226,8 @@ fd_status fd_decode(const void *q, const void *k, const void *v, void *o,
  *                are never read (padding such as -1 is fine). Entries that are
  *                read must lie in [0, num_pages); others are clamped into that
  *                range (that sequence's output is then unspecified, but no
- *                access leaves the cache).
+ *                access leaves the cache), and fd_options.debug_checks turns
+ *                them into FD_ERR_BAD_DATA.
  *   seq_lens     [B] int32, device; L_b, clamped to [0, min(max_seq_len,
  *                max_blocks * page_size)]; L_b == 0 gives o[b] = 0.
  *   page_size    tokens per page, a power of two in [1, 1024]

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("fd_decode", "fd_paged_decode", "fd_decode_fp8kv", "fd_paged_decode_fp8kv", "fd_decode_plan",
-                     "fd_paged_plan", "fd_status_string", "fd_last_error", "fd_device_num_cus"):
+                     "fd_paged_plan", "fd_decode_workspace_size", "fd_paged_workspace_size", "fd_status_string",
+                     "fd_last_error", "fd_device_num_cus"):
         assert required in names
 
 
@@ -37,9 +38,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = fd.lib()
-    names = [lib.fd_status_string(i).decode() for i in range(6)]
+    names = [lib.fd_status_string(i).decode() for i in range(7)]
     assert names == ["FD_OK", "FD_ERR_INVALID_ARG", "FD_ERR_UNSUPPORTED", "FD_ERR_WORKSPACE", "FD_ERR_DEVICE",
-                     "FD_ERR_LAUNCH"]
+                     "FD_ERR_LAUNCH", "FD_ERR_BAD_DATA"]
     assert lib.fd_status_string(99).decode() == "FD_ERR_UNKNOWN"
 
 
@@ -157,7 +158,7 @@ def test_plan_rejects(kw, status):
 
 def test_options_are_validated():
     for opt in (fd.options(force_chunk=100), fd.options(force_num_splits=-1), fd.options(kernel=5),
-                binding.FdOptions(0, 0, 0, 1, None, None)):
+                binding.FdOptions(0, 0, 0, 2, None, None), fd.options(debug_checks=-1)):
         with pytest.raises(fd.FdError) as e:
             fd.decode_plan(8, 8, 512, "f32", 256, opt)
         assert e.value.name == "FD_ERR_INVALID_ARG"
@@ -274,3 +275,65 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         binding.lib()
     with pytest.raises(RuntimeError, match="missing"):
         fd.decode_plan(8, 8, 512, "f32", 256)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workspace_size_calls_match_the_plans(name):
+    """fd_decode_workspace_size / fd_paged_workspace_size return the plan's
+    workspace_bytes, with and without forced shapes and the debug record."""
+    w = WORKLOADS[name]
+    for opt in (None, fd.options(force_num_splits=3), fd.options(force_chunk=128), fd.options(debug_checks=1)):
+        if w.kind == "single":
+            p = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 256, opt)
+            assert fd.decode_workspace_size(w.H, w.Hkv, w.S, w.dtype, 256, opt) == p["workspace_bytes"]
+        else:
+            L = w.seq_lens()
+            args = (w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+            p = fd.paged_plan(*args, opt)
+            assert fd.paged_workspace_size(*args, opt) == p["workspace_bytes"]
+    with pytest.raises(fd.FdError) as e:
+        fd.decode_workspace_size(8, 8, 512, "f32", 256, fd.options(force_chunk=100))
+    assert e.value.name == "FD_ERR_INVALID_ARG"
+    assert fd.lib().fd_decode_workspace_size(8, 8, 512, 128, 0, 256, None, None) == 1  # NULL out pointer
+
+
+def test_debug_record_in_the_paged_plan():
+    """debug_checks adds a 16-byte record, 256-byte aligned, after the partials of a
+    paged plan (also when the plan has no partials); contiguous plans are unchanged."""
+    for max_len, total in ((8192, 300000), (100, 1000)):
+        a = fd.paged_plan(64, 32, 8, "bf16", 16, max_len, total, 256)
+        b = fd.paged_plan(64, 32, 8, "bf16", 16, max_len, total, 256, fd.options(debug_checks=1))
+        assert a["ws_err_offset"] == 0
+        assert b["ws_err_offset"] >= a["workspace_bytes"] and b["ws_err_offset"] % 256 == 0
+        assert b["workspace_bytes"] == b["ws_err_offset"] + 16
+        assert {k: v for k, v in a.items() if k not in ("workspace_bytes", "ws_err_offset")} == \
+            {k: v for k, v in b.items() if k not in ("workspace_bytes", "ws_err_offset")}
+    assert fd.decode_plan(32, 32, 4096, "bf16", 256) == fd.decode_plan(32, 32, 4096, "bf16", 256,
+                                                                         fd.options(debug_checks=1))
+
+
+def test_merge_choice():
+    """Multi-split plans merge with the merge kernel unless the fused merge (the last
+    workgroups merge, one launch) is asked for; it is available up to 32 splits per
+    sequence on the full grid, and asking for it elsewhere is refused."""
+    for name in ("decode_f32_h8_s512", "decode_bf16_h32_s4096", "decode_bf16_h32_s131072_peaked"):
+        w = WORKLOADS[name]
+        p = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 256)
+        assert p["merge"] == 1 and p["num_splits"] <= 32, (name, p)
+        assert p["ws_o_offset"] == binding.WS_COUNTER_BYTES
+        f = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 256, fd.options(merge="fused"))
+        assert f["merge"] == 2 and {k: v for k, v in f.items() if k != "merge"} == \
+            {k: v for k, v in p.items() if k != "merge"}
+    p = fd.decode_plan(8, 8, 40000, "bf16", 256, fd.options(force_chunk=64))
+    assert p["num_splits"] > 32 and p["merge"] == 1
+    with pytest.raises(fd.FdError) as e:
+        fd.decode_plan(8, 8, 40000, "bf16", 256, fd.options(force_chunk=64, merge="fused"))
+    assert e.value.name == "FD_ERR_UNSUPPORTED"
+    for name in ("paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"):
+        w = WORKLOADS[name]
+        L = w.seq_lens()
+        p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+        assert p["merge"] == 1
+    assert fd.decode_plan(8, 8, 100, "f32", 256, fd.options(force_num_splits=1))["merge"] == 0
+    with pytest.raises(fd.FdError):
+        fd.decode_plan(8, 8, 512, "f32", 256, fd.options(merge=3))

@@ -170,32 +170,26 @@ def test_workload_bf16_h32_s4096(device):
     assert_close(single(d, device), ref_single(d), w.name)
 
 
-def test_workload_s131072_sampled(device):
+def test_workload_s131072(device):
+    """The 128k-token peaked decode over an E4M3 cache, all 32 heads."""
     w = inputs.WORKLOADS["decode_bf16_h32_s131072_peaked"]
     d = inputs.with_fp8_kv(w.make())
     announce(w.name)
-    o = single(d, device)
-    assert torch.isfinite(o.float()).all()
-    heads = [1, 9, 30]
-    assert_close(o[heads], ref_single(d, heads=heads), w.name)
+    assert_close(single(d, device), ref_single(d), w.name)
 
 
-def test_paged_workload(device):
-    """The B=64 GQA-4 paged batch with E4M3 caches; sampled (sequence, head) pairs,
-    the shortest and longest sequences included, both kernels."""
-    w = inputs.WORKLOADS["paged_gqa4_bf16_b64_s1k-8k"]
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"])
+def test_paged_workload(name, device):
+    """The GQA-4 (B = 64) and GQA-8 (B = 128, work list) paged batches with E4M3
+    caches, every (sequence, head) row, both kernels."""
+    w = inputs.WORKLOADS[name]
     announce(f"{w.name} (generating inputs)")
     d = inputs.with_fp8_kv(w.make())
-    lens = d["seq_lens"].numpy()
-    rng = np.random.default_rng(340)
-    bs = sorted({int(np.argmin(lens)), int(np.argmax(lens))} | set(rng.choice(w.B, 5, replace=False).tolist()))
-    pairs = [(b, int(h)) for b in bs for h in rng.choice(w.H, 3, replace=False)]
-    ref = ref_paged(d, pairs=pairs)
+    ref = ref_paged(d)
     for kernel in ("auto", "valu"):
         announce(f"{w.name} {kernel}")
-        o = paged(d, device, opt=fd.options(kernel=kernel))
-        assert torch.isfinite(o.float()).all()
-        assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, f"{w.name} {kernel}")
+        assert_close(paged(d, device, opt=fd.options(kernel=kernel)), ref, f"{w.name} {kernel}")
 
 
 # ------------------------------------------------------------------ paged addressing

@@ -51,6 +51,59 @@ def assert_close(got, ref, dtype: str, what: str = ""):
     return err.max()
 
 
+U32 = 2.0 ** -24  # fp32 unit roundoff
+D = 128
+
+
+def lse_atol(q_row, keys, scale: float) -> float:
+    """Bound on |lse_gpu - lse| for one split, from the kernel's fp32 arithmetic.
+
+    Each score is a D-term fp32 dot product of exactly representable products, off
+    by at most gamma_D * |scale| * sum_d |q_d k_td| (gamma_D = D u / (1 - D u),
+    u = 2^-24), and is scaled once more in fp32 (u |s|); a log-sum-exp moves by at
+    most its largest score error. The running sum l of L terms 2^(x - m) (each from
+    v_exp_f32, within 1 ulp) is off by a relative (L + 2) u, so ln l by that much;
+    m + log2 l and the final multiplication by ln 2 add 3 u |lse|.
+    """
+    q = np.asarray(q_row, np.float64)
+    k = np.asarray(keys, np.float64)
+    L = k.shape[0]
+    if L == 0:
+        return 0.0
+    dots = np.abs(k) @ np.abs(q) * abs(scale)
+    s = k @ q * scale
+    m = s.max()
+    lse = m + np.log(np.exp(s - m).sum())
+    gamma = D * U32 / (1 - D * U32)
+    return float(gamma * dots.max() + U32 * np.abs(s).max() + (L + 2) * U32 + 3 * U32 * abs(lse))
+
+
+def assert_lse_close(got, ref, atols, what=""):
+    got = np.asarray(got.detach().cpu().numpy() if hasattr(got, "detach") else got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    bad = ~(err <= np.asarray(atols))
+    assert not bad.any(), f"{what}: lse max|err| {err.max():.3e}, {int(bad.sum())}/{bad.size} above the fp32 bound"
+
+
+def _f64(x):
+    return x.detach().to(torch.float64).numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+
+
+def split_lse_atols(q_row, k_rows, scale, bounds):
+    """lse_atol of every split [a, b) of one head's key rows k_rows [L, D]."""
+    return [lse_atol(q_row, k_rows[a:b], scale) for a, b in bounds]
+
+
+def poisoned_workspace(nbytes: int, dev) -> torch.Tensor:
+    """A workspace filled with NaN except its counter block, which every call needs
+    zero on first use: a partial the call did not write shows up as NaN."""
+    ws = torch.full((max(nbytes, fd.binding.WS_COUNTER_BYTES) // 4 + 1,), float("nan"), dtype=torch.float32,
+                    device=dev).view(torch.uint8)
+    ws[:fd.binding.WS_COUNTER_BYTES].zero_()
+    return ws
+
+
 def to_dev(d: dict, dev) -> dict:
     return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
@@ -147,18 +200,13 @@ def long_peaked():
     return inputs.WORKLOADS["decode_bf16_h32_s131072_peaked"].make()
 
 
-SAMPLED_HEADS = [0, 5, 13, 22, 31]
-
-
 def test_workload_bf16_h32_s131072_peaked(device, long_peaked):
-    """Full size, the launch the benchmark times; sampled heads against the oracle,
-    every head checked for finiteness."""
+    """Full size, the launch the benchmark times; all 32 heads against the oracle."""
     d = long_peaked
     announce("decode_bf16_h32_s131072_peaked")
     o = run_single(d, device)
-    assert torch.isfinite(o.float()).all()
-    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=SAMPLED_HEADS)
-    assert_close(o[SAMPLED_HEADS], ref, "bf16", "s131072 sampled heads")
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    assert_close(o, ref, "bf16", "s131072 all heads")
 
 
 def test_partials_of_long_peaked(device, long_peaked):
@@ -171,10 +219,14 @@ def test_partials_of_long_peaked(device, long_peaked):
     announce(f"s131072 partials chunk {plan['chunk']} splits {plan['num_splits']}")
     run_single(d, device, ws=ws)
     ws_o, ws_lse = fd.workspace_views(ws, plan, 1, 32)
+    bounds = kernel_split_bounds(d["S"], plan["chunk"])
+    assert len(bounds) == plan["num_splits"]
     for h in (3, 27):
-        O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], plan["chunk"], heads=[h])
+        O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], plan["chunk"], heads=[h],
+                                           bounds=bounds)
         assert_close(ws_o[0, h], O_s[0], "bf16", f"partials head {h}")
-        np.testing.assert_allclose(ws_lse[0, h].cpu().numpy(), lse_s[0], rtol=1e-5, atol=5e-4)
+        atols = split_lse_atols(_f64(d["q"][h]), _f64(d["k"][:, h]), d["scale"], bounds)
+        assert_lse_close(ws_lse[0, h], lse_s[0], atols, f"partials head {h}")
 
 
 def kernel_split_bounds(L: int, chunk: int) -> list:
@@ -191,7 +243,7 @@ def test_partials_last_split_takes_the_remainder(kernel, device):
     d = inputs.single_inputs(8, 2, 1000, 128, "bf16", 95, peak_frac=0.01)
     opt = fd.options(force_chunk=64, kernel=kernel)
     plan = fd.decode_plan(8, 2, 1000, "bf16", 0, opt)
-    assert plan["num_splits"] == 15 and plan["merge"] == 1
+    assert plan["num_splits"] == 15 and plan["merge"] != 0
     ws = fd.new_workspace(plan["workspace_bytes"], device)
     announce(f"remainder partials {kernel}")
     o = run_single(d, device, opt=opt, ws=ws)
@@ -201,7 +253,8 @@ def test_partials_last_split_takes_the_remainder(kernel, device):
     O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], 64, bounds=bounds)
     for h in range(8):
         assert_close(ws_o[0, h], O_s[h], "bf16", f"partials head {h}")
-        np.testing.assert_allclose(ws_lse[0, h].cpu().numpy(), lse_s[h], rtol=1e-5, atol=5e-4)
+        atols = split_lse_atols(_f64(d["q"][h]), _f64(d["k"][:, h // 4]), d["scale"], bounds)
+        assert_lse_close(ws_lse[0, h], lse_s[h], atols, f"partials head {h}")
     ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
     assert_close(o, ref, "bf16", "merged")
 
@@ -213,23 +266,21 @@ def _sample_pairs(B, H, lens, n, seed):
     return [(b, int(h)) for b in bs for h in rng.choice(H, size=3, replace=False)]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"])
 def test_paged_workloads(name, device):
-    """Full size in the benchmark's launch (matrix-core kernel), then the vector-ALU
-    kernel forced; sampled (sequence, head) pairs against the oracle, including the
-    shortest and the longest sequence."""
+    """Full size in the benchmark's launch (matrix-core kernel, the work list for the
+    GQA8 batch), then the vector-ALU kernel forced; every (sequence, head) row
+    against the oracle."""
     w = inputs.WORKLOADS[name]
     announce(f"{name} (generating inputs)")
     d = w.make()
-    pairs = _sample_pairs(w.B, w.H, d["seq_lens"].numpy(), 6, 3)
     ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
-                                           d["page_size"], d["scale"], pairs=pairs)
+                                           d["page_size"], d["scale"])
     for kernel in ("auto", "valu"):
         announce(f"{name} run {kernel}")
         o = run_paged(d, device, opt=fd.options(kernel=kernel))
-        assert torch.isfinite(o.float()).all()
-        got = torch.stack([o[b, h] for b, h in pairs])
-        assert_close(got, ref, w.dtype, f"{name} {kernel}")
+        assert_close(o, ref, w.dtype, f"{name} {kernel}")
 
 
 # ------------------------------------------------------------------ invariance and tails
@@ -407,14 +458,15 @@ def test_many_splits(H, Hkv, S, chunk, device):
 
 
 def test_workspace_reuse_across_plans(device):
-    """One uninitialised workspace (filled with NaN) serves calls of different plans in
-    any order: nothing is read from it that the same call did not write."""
+    """One workspace (filled with NaN but for its zeroed counter block) serves calls of
+    different plans in any order, fused and merge-kernel ones alike: nothing is read
+    from it that the same call did not write, and every call leaves the counters zero."""
     cases = [inputs.single_inputs(8, 8, S, 128, "bf16", 200 + S) for S in (4099, 1000, 8191)]
     refs = [oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])[0] for d in cases]
     plans = [(i, c) for i in range(3) for c in (64, 256, 1024)]
     need = max(fd.decode_plan(8, 8, cases[i]["S"], "bf16", 0, fd.options(force_chunk=c))["workspace_bytes"]
                for i, c in plans)
-    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=device).view(torch.uint8)
+    ws = poisoned_workspace(need, device)
     rng = np.random.default_rng(7)
     for k in rng.permutation(len(plans)).tolist() + rng.permutation(len(plans)).tolist():
         i, c = plans[k]
@@ -599,3 +651,221 @@ def test_paged_long_sequence(device):
     ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
                                            16, d["scale"], pairs=pairs)
     assert_close(torch.stack([o[b, h] for b, h in pairs]), ref, "bf16", "paged 128k")
+
+
+# ------------------------------------------------------------------ paged partials, sweep lengths
+
+
+@pytest.mark.parametrize("work_list", [True, False])
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_paged_partials(kernel, work_list, device):
+    """The paged split kernels alone: ws_o / ws_lse of every split of every (sequence,
+    head) of a ragged batch on shuffled pages, against the oracle's paged partials over
+    the library's token ranges; with the numbered work list (total_kv given) and with
+    the full grid. The workspace starts NaN-filled, so an unwritten partial shows."""
+    lens = [5, 300, 1500, 4000, 2049, 0, 64, 3333]
+    B, H, Hkv, chunk = len(lens), 32, 8, 256
+    d = inputs.paged_inputs(B, H, Hkv, 128, "bf16", 16, lens, 960)
+    opt = fd.options(force_chunk=chunk, kernel=kernel)
+    total = sum(lens) if work_list else 0
+    plan = fd.paged_plan(B, H, Hkv, "bf16", 16, max(lens), total, 0, opt)
+    assert plan["work_list"] == int(work_list) and plan["merge"] == 1 and plan["chunk"] == chunk
+    ws = poisoned_workspace(plan["workspace_bytes"], device)
+    g = to_dev(d, device)
+    announce(f"paged partials {kernel} work_list={work_list}")
+    o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                           scale=d["scale"], max_seq_len=max(lens), total_kv=total, opt=opt, ws=ws)
+    torch.cuda.synchronize()
+    ws_o, ws_lse = fd.workspace_views(ws, plan, B, H)
+    checked = 0
+    for b, L in enumerate(lens):
+        bounds = kernel_split_bounds(L, chunk)
+        if len(bounds) <= 1:
+            continue  # one split: written to o directly
+        kb = oracle.gather_pages(d["k_cache"], d["block_table"][b], L, 16)
+        for h in range(H):
+            O_s, lse_s = oracle.paged_split_partials(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                                     d["seq_lens"], 16, d["scale"], chunk, b, h, bounds=bounds)
+            n = len(bounds)
+            assert_close(ws_o[b, h, :n], O_s, "bf16", f"partials b={b} h={h}")
+            atols = split_lse_atols(_f64(d["q"][b, h]), _f64(kb[:, h // 4]), d["scale"], bounds)
+            assert_lse_close(ws_lse[b, h, :n], lse_s, atols, f"partials b={b} h={h}")
+            checked += n
+    assert checked > 0
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"])
+    assert_close(o, ref, "bf16", f"paged partials merged {kernel}")
+
+
+SWEEP_HEADS = [0, 1, 14, 30, 31]  # both heads of the first and the last KV-head pair
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("S", [8192, 16384, 32768, 65536, 131073])
+def test_sweep_length_full_size(S, device):
+    """The KV-length curve the benchmark times (32 heads, bf16) at full size in its own
+    launch: five heads against the oracle, every head finite; at 131073 tokens (the
+    pages' odd length) the last split holds chunk + 1 tokens, and the workspace
+    partials of two heads, that split included, are checked as well."""
+    w = inputs.sweep_workload(S)
+    d = w.make()
+    plan = fd.decode_plan(32, 32, S, "bf16")
+    ws = poisoned_workspace(plan["workspace_bytes"], device)
+    announce(f"sweep S={S} chunk {plan['chunk']} splits {plan['num_splits']}")
+    o = run_single(d, device, ws=ws)
+    assert torch.isfinite(o.float()).all()
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"], heads=SWEEP_HEADS)
+    assert_close(o[SWEEP_HEADS], ref, "bf16", f"S={S}")
+    if S == 131073:
+        bounds = kernel_split_bounds(S, plan["chunk"])
+        assert plan["merge"] != 0 and bounds[-1][1] - bounds[-1][0] == plan["chunk"] + 1
+        ws_o, ws_lse = fd.workspace_views(ws, plan, 1, 32)
+        for h in (1, 30):
+            O_s, lse_s = oracle.split_partials(d["q"], d["k"], d["v"], d["scale"], plan["chunk"], heads=[h],
+                                               bounds=bounds)
+            assert_close(ws_o[0, h], O_s[0], "bf16", f"S={S} partials head {h}")
+            atols = split_lse_atols(_f64(d["q"][h]), _f64(d["k"][:, h]), d["scale"], bounds)
+            assert_lse_close(ws_lse[0, h], lse_s[0], atols, f"S={S} partials head {h}")
+
+
+# ------------------------------------------------------------------ device-data checks
+
+
+@pytest.mark.parametrize("work_list", [True, False])
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+def test_debug_checks_report_bad_table_and_lengths(kernel, work_list, device):
+    """fd_options.debug_checks: a clean batch gives the same output bit for bit as
+    without it; a table entry outside [0, num_pages) inside a sequence's pages, or a
+    negative length, comes back as FD_ERR_BAD_DATA naming the sequence and index.
+    The -1 padding past each sequence's pages is never reported. Without the checks
+    the bad entry is clamped (no access leaves the cache) and the other sequences
+    are unchanged."""
+    lens = [5, 300, 1500, 4000]
+    d = inputs.paged_inputs(4, 32, 8, 128, "bf16", 16, lens, 970)
+    assert (d["block_table"] == -1).any()  # padded rows
+    g = to_dev(d, device)
+    total = sum(lens) if work_list else 0
+
+    def call(debug, table=None, seq_lens=None):
+        opt = fd.options(force_chunk=256, kernel=kernel, debug_checks=debug)
+        o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"] if table is None else table,
+                               g["seq_lens"] if seq_lens is None else seq_lens, 16, scale=d["scale"],
+                               max_seq_len=max(lens), total_kv=total, opt=opt)
+        torch.cuda.synchronize()
+        return o.cpu()
+
+    plan = fd.paged_plan(4, 32, 8, "bf16", 16, max(lens), total, 0, fd.options(force_chunk=256, kernel=kernel))
+    assert plan["work_list"] == int(work_list)
+    announce(f"debug checks {kernel} work_list={work_list}: clean")
+    clean = call(False)
+    assert torch.equal(call(True), clean)
+    bad = d["block_table"].clone()
+    bad[2, 40] = d["num_pages"] + 7
+    bad_dev = bad.to(device)
+    announce(f"debug checks {kernel} work_list={work_list}: bad entry")
+    with pytest.raises(fd.FdError) as e:
+        call(True, table=bad_dev)
+    assert e.value.name == "FD_ERR_BAD_DATA" and f"block_table[2][40] = {d['num_pages'] + 7}" in str(e.value)
+    neg = d["block_table"].clone()
+    neg[1, 3] = -1
+    with pytest.raises(fd.FdError) as e:
+        call(True, table=neg.to(device))
+    assert "block_table[1][3] = -1" in str(e.value)
+    lens_bad = d["seq_lens"].clone()
+    lens_bad[3] = -5
+    announce(f"debug checks {kernel} work_list={work_list}: bad length")
+    with pytest.raises(fd.FdError) as e:
+        call(True, seq_lens=lens_bad.to(device))
+    assert e.value.name == "FD_ERR_BAD_DATA" and "seq_lens[3] = -5" in str(e.value)
+    announce(f"debug checks {kernel} work_list={work_list}: bad entry, checks off")
+    o = call(False, table=bad_dev)
+    for b in (0, 1, 3):
+        assert torch.equal(o[b], clean[b])
+
+
+# ------------------------------------------------------------------ fused merge
+
+
+FUSED_CASES = [  # (H, Hkv, S, dtype, kernel, chunk); at most 64 (head, split) rows per workgroup
+    (8, 8, 512, "f32", "auto", 0),        # the 512-token fp32 decode's own plan: 32 splits of 16
+    (32, 32, 4096, "bf16", "auto", 0),    # the 4k decode's own plan
+    (32, 32, 4099, "bf16", "auto", 256),  # ragged last split
+    (32, 4, 3000, "bf16", "auto", 448),   # 8 heads per KV head on the matrix cores: 6 splits
+    (32, 4, 3000, "f16", "valu", 448),    # the same on the vector ALUs (8 heads per workgroup)
+    (64, 4, 2048, "bf16", "auto", 1024),  # 16 heads per workgroup, 2 splits
+    (12, 3, 777, "f32", "auto", 64),      # fp32 GQA
+]
+
+
+@pytest.mark.parametrize("H,Hkv,S,dtype,kernel,chunk", FUSED_CASES)
+def test_fused_and_kernel_merge_agree(H, Hkv, S, dtype, kernel, chunk, device):
+    """The one-launch step (the last workgroup of each head slice merges) and the
+    two-launch step (a merge kernel) on the same plan: both against the oracle, and
+    the partials they leave in the workspace are the same bits."""
+    d = inputs.single_inputs(H, Hkv, S, 128, dtype, 990 + S + H)
+    ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+    outs, parts = {}, {}
+    for merge in ("fused", "kernel"):
+        opt = fd.options(force_chunk=chunk, kernel=kernel, merge=merge)
+        plan = fd.decode_plan(H, Hkv, S, dtype, 0, opt)
+        assert plan["merge"] == {"fused": 2, "kernel": 1}[merge]
+        ws = poisoned_workspace(plan["workspace_bytes"], device)
+        announce(f"fused/kernel merge {merge} H={H} Hkv={Hkv} S={S} {dtype} splits {plan['num_splits']}")
+        outs[merge] = run_single(d, device, opt=opt, ws=ws).cpu()
+        assert_close(outs[merge], ref, dtype, f"{merge} merge")
+        wo, wl = fd.workspace_views(ws, plan, 1, H)
+        parts[merge] = (wo.cpu(), wl.cpu())
+        assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)  # counters left at zero
+    assert torch.equal(parts["fused"][0], parts["kernel"][0]) and torch.equal(parts["fused"][1], parts["kernel"][1])
+
+
+def test_fused_merge_repeated_calls(device):
+    """Forty fused calls on one workspace, alternating two inputs of the same plan:
+    every output is bit-identical to the first output of its input, so no call ever
+    merges a partial left by the call before it."""
+    ds = [inputs.single_inputs(32, 32, 4096, 128, "bf16", 995 + i) for i in range(2)]
+    gs = [to_dev(d, device) for d in ds]
+    opt = fd.options(merge="fused")
+    plan = fd.decode_plan(32, 32, 4096, "bf16", 0, opt)
+    assert plan["merge"] == 2
+    ws = fd.new_workspace(plan["workspace_bytes"], device)
+    announce("fused repeated calls")
+    first = [None, None]
+    outs = []
+    for i in range(40):
+        g = gs[i % 2]
+        outs.append(fd.fd_decode(g["q"], g["k"], g["v"], scale=ds[0]["scale"], ws=ws, opt=opt))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        if first[i % 2] is None:
+            first[i % 2] = o.cpu()
+        assert torch.equal(o.cpu(), first[i % 2]), i
+    for j, d in enumerate(ds):
+        ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
+        assert_close(first[j], ref, "bf16", f"input {j}")
+
+
+def test_fused_paged_grid(device):
+    """A paged batch on the full (split, sequence) grid with the fused merge forced
+    (counters per sequence and head slice), against the oracle; a work-list plan
+    cannot fuse and says so."""
+    lens = [5, 300, 1500, 4000, 2049, 0, 64, 3333]
+    d = inputs.paged_inputs(len(lens), 32, 8, 128, "bf16", 16, lens, 997)
+    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                                           16, d["scale"])
+    g = to_dev(d, device)
+    for kernel in ("mfma", "valu"):
+        opt = fd.options(force_chunk=256, kernel=kernel, merge="fused")
+        plan = fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), 0, 0, opt)
+        assert plan["merge"] == 2 and plan["work_list"] == 0
+        ws = poisoned_workspace(plan["workspace_bytes"], device)
+        announce(f"fused paged grid {kernel}")
+        o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                               scale=d["scale"], max_seq_len=max(lens), total_kv=0, opt=opt, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(o, ref, "bf16", f"fused paged {kernel}")
+        assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)
+    with pytest.raises(fd.FdError) as e:
+        fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), sum(lens), 0,
+                      fd.options(force_chunk=256, merge="fused"))
+    assert e.value.name == "FD_ERR_UNSUPPORTED"
