@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     fd_decode,
     fd_decode_fp8kv,
     fd_paged_decode,
+    fd_paged_decode_noalloc,
     fd_paged_decode_fp8kv,
     fd_prefill,
     lib,

@@ -26,6 +26,7 @@ FP8_CACHE_DTYPES = (torch.float8_e4m3fn, torch.uint8)  # uint8 = raw E4M3 codes
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "kernel": 1, "fused": 2}
 WS_COUNTER_BYTES = 16384  # zeroed head block of every workspace (include/fd.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of fd_paged_decode_noalloc (include/fd.h)
 HEAD_DIM = 128
 CHUNK_QUANTUM = 64
 
@@ -75,6 +76,11 @@ SIGNATURES = {
                                        ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(FdOptions),
                                        ctypes.c_void_p]),
+    "fd_paged_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_float,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                                               ctypes.POINTER(FdOptions), ctypes.c_void_p]),
     "fd_decode_fp8kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
@@ -320,6 +326,23 @@ def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                                  seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
                                  num_pages, max_blocks, max_seq_len, int(total_kv), dt, wp or None, wb,
                                  _opt_ptr(opt), _stream_handle(stream)))
+    return o
+
+
+def fd_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, page_size: int | None = None, o: torch.Tensor | None = None,
+                            scale: float | None = None, max_seq_len: int | None = None, total_kv: int = 0,
+                            opt: FdOptions | None = None, stream=None) -> torch.Tensor:
+    """``fd_paged_decode`` on the library's static per-GPU scratch (no workspace is
+    allocated); calls that overlap on one GPU race on that scratch."""
+    B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
+        q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib().fd_paged_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                         seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
+                                         num_pages, max_blocks, max_seq_len, int(total_kv), _dtype_code(q.dtype),
+                                         _opt_ptr(opt), _stream_handle(stream)))
     return o
 
 

@@ -307,8 +307,13 @@ fd_status debug_verdict(const int32_t *err, hipStream_t stream) {
 }
 
 fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a, fd::MergeArgs &m, int B,
-              void *ws, size_t ws_bytes, const fd_options *opt, hipStream_t stream) {
+              void *ws, size_t ws_bytes, const fd_options *opt, hipStream_t stream, bool static_ws = false) {
     if (plan.workspace_bytes > 0) {
+        if (static_ws && ws_bytes < plan.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE,
+                        "this call needs %zu bytes of workspace, more than the library's static scratch of %zu "
+                        "bytes: pass a larger fd_options.force_chunk (fewer splits), or call fd_paged_decode "
+                        "with a workspace", plan.workspace_bytes, ws_bytes);
         if (ws == nullptr || ws_bytes < plan.workspace_bytes)
             return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", plan.workspace_bytes, ws_bytes,
                         ws == nullptr ? " (NULL)" : "");
@@ -469,7 +474,8 @@ fd_status decode_impl(const void *q, const void *k, const void *v, void *o, int 
 fd_status paged_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
                      const int32_t *seq_lens, int page_size, void *o, float scale, float k_scale, float v_scale,
                      int B, int H, int Hkv, int D, int num_pages, int max_blocks, int max_seq_len, long long total_kv,
-                     fd_dtype dtype, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {
+                     fd_dtype dtype, void *ws, size_t ws_bytes, const fd_options *opt, void *stream,
+                     bool static_ws = false) {
     fd_status s = check_common(B, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
     if ((s = check_score_scale(scale, k_scale)) != FD_OK) return s;
@@ -511,12 +517,62 @@ fd_status paged_impl(const void *q, const void *k_cache, const void *v_cache, co
     m.out = o;
     m.H = H;
     m.max_len = eff_max;
-    return run(plan, dtype, true, a, m, B, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream));
+    return run(plan, dtype, true, a, m, B, ws, ws_bytes, opt, reinterpret_cast<hipStream_t>(stream), static_ws);
+}
+
+// Static scratch of fd_paged_decode_noalloc: a device array every GPU the
+// library runs on holds until the process ends. In host code `scratch` only
+// names the array (it is not a device address): its address on the current
+// device comes from hipGetSymbolAddress, taken once per device and kept in
+// g_scratch_ptr, and only that pointer is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[FD_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+std::vector<void *> g_scratch_ptr;
+
+__global__ void zero_words_kernel(unsigned *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The scratch address on the current device. The first call on a device looks it
+// up and clears the counter block at its head with a fill kernel on `stream`
+// (a kernel, not a memset, so that the call may be captured into a graph).
+fd_status scratch_of_current_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(FD_ERR_DEVICE, "no current HIP device");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(FD_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, stream, reinterpret_cast<unsigned *>(p),
+                           (int)(FD_WS_COUNTER_BYTES / sizeof(unsigned)));
+        const hipError_t le = hipGetLastError();
+        if (le != hipSuccess) return fail(FD_ERR_LAUNCH, "clearing the scratch counters: %s", hipGetErrorString(le));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FD_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+fd_status fd_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *seq_lens, int page_size, void *o,
+                                  float scale, int B, int H, int Hkv, int D, int num_pages, int max_blocks,
+                                  int max_seq_len, long long total_kv, fd_dtype dtype, const fd_options *opt,
+                                  void *stream) {
+    if (fd::is_fp8_cache(dtype)) return fail(FD_ERR_UNSUPPORTED, "FP8 KV caches go through fd_paged_decode_fp8kv");
+    void *ws = nullptr;
+    const fd_status s = scratch_of_current_device(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (s != FD_OK) return s;
+    return paged_impl(q, k_cache, v_cache, block_table, seq_lens, page_size, o, scale, 1.f, 1.f, B, H, Hkv, D,
+                      num_pages, max_blocks, max_seq_len, total_kv, dtype, ws, FD_NOALLOC_SCRATCH_BYTES, opt, stream,
+                      true);
+}
 
 fd_status fd_decode(const void *q, const void *k, const void *v, void *o, int H, int Hkv, int S, int D,
                     fd_dtype dtype, float scale, void *ws, size_t ws_bytes, const fd_options *opt, void *stream) {

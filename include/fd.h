@@ -46,6 +46,7 @@ extern "C" {
 #define FD_HEAD_DIM 128
 #define FD_CHUNK_QUANTUM 64 /* a forced chunk must be a positive multiple of this */
 #define FD_WS_COUNTER_BYTES 16384 /* counter block at the head of every workspace (see the layout below) */
+#define FD_NOALLOC_SCRATCH_BYTES (64u << 20) /* the static scratch of fd_paged_decode_noalloc, per GPU */
 
 typedef enum fd_dtype {
     FD_DTYPE_F32 = 0,
@@ -247,6 +248,30 @@ fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cach
                           void *o, float scale, int B, int H, int Hkv, int D, int num_pages,
                           int max_blocks, int max_seq_len, long long total_kv, fd_dtype dtype,
                           void *ws, size_t ws_bytes, const fd_options *opt, void *stream);
+
+/*
+ * fd_paged_decode without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. Arguments, plan and results are those of
+ * fd_paged_decode without ws / ws_bytes. Nothing is allocated, by the call or
+ * by any routine it calls: the partials (and counters, and the debug record)
+ * live in a static device array of FD_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends.
+ *   - A call whose plan needs more (fd_plan.workspace_bytes of fd_paged_plan)
+ *     returns FD_ERR_WORKSPACE before launching anything; a larger
+ *     fd_options.force_chunk (fewer splits) shrinks the need.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *     contents. Calls that overlap on one GPU (different streams or threads)
+ *     RACE on it: the caller must order them.
+ *   - The first call on a device also launches a small fill kernel on `stream`
+ *     that zeroes the counter block at the head of the array.
+ * Errors as for fd_paged_decode.
+ */
+fd_status fd_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_table, const int32_t *seq_lens, int page_size, void *o,
+                                  float scale, int B, int H, int Hkv, int D, int num_pages, int max_blocks,
+                                  int max_seq_len, long long total_kv, fd_dtype dtype, const fd_options *opt,
+                                  void *stream);
 
 /*
  * FP8 KV cache. "FlashAttention 与推理算子", in the improvements listed after its
