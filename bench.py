@@ -79,7 +79,7 @@ class Case:
     """A workload placed in device memory with rotated KV copies and its C-ABI arguments."""
 
     def __init__(self, w, chunk: int = 0, kernel: str = "auto", data: dict | None = None, kv: str = "native",
-                 merge: str = "auto"):
+                 merge: str = "auto", launch: str = "auto"):
         import torch
 
         import decode_attention_13_amd as fd
@@ -98,8 +98,8 @@ class Case:
             data = with_fp8_kv(data)
         d = data
         self.d = d
-        forced = chunk or kernel != "auto" or merge != "auto"
-        self.opt = fd.options(force_chunk=chunk, kernel=kernel, merge=merge) if forced else None
+        forced = chunk or kernel != "auto" or merge != "auto" or launch != "auto"
+        self.opt = fd.options(force_chunk=chunk, kernel=kernel, merge=merge, launch=launch) if forced else None
         qdt = inputs_dtype(w.dtype)
         esize = 1 if self.fp8 else torch.tensor([], dtype=qdt).element_size()
         self.dtype_code = binding.FD_DTYPE_KV_E4M3[qdt] if self.fp8 else binding.FD_DTYPE[qdt]
@@ -190,6 +190,7 @@ def time_steps(case: Case, steps: int, warmup: int) -> dict:
                             force_chunk=base.force_chunk if base else 0,
                             kernel=base.force_kernel if base else 0,
                             merge=base.force_merge if base else 0,
+                            launch=base.force_launch if base else 0,
                             split_begin_event=begins[i], split_end_event=ends[i]) for i in range(steps)]
     torch.cuda.synchronize()
     for i in range(warmup):  # back to steady state after the synchronisations
@@ -447,6 +448,8 @@ def main() -> int:
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"], help="force the split kernel")
     ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "fused"],
                     help="force how split partials are merged (merge kernel, or the last workgroups)")
+    ap.add_argument("--launch", default="auto", choices=["auto", "grid", "persistent"],
+                    help="paged workloads: a workgroup per item, or one per resident slot claiming items")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="cache storage: the workload's dtype, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--sweep", action="store_true",
@@ -474,7 +477,7 @@ def main() -> int:
         print(json.dumps(bench_prefill(args)), flush=True)
         return 0
     w = WORKLOADS[args.workload]
-    case = Case(w, args.chunk, args.kernel, kv=args.kv, merge=args.merge)
+    case = Case(w, args.chunk, args.kernel, kv=args.kv, merge=args.merge, launch=args.launch)
     split_kernel = SPLIT_KERNELS[case.plan["kernel"]]
     wl_name = w.name + ("_kv_e4m3" if case.fp8 else "")
     t = time_steps(case, args.steps, args.warmup)

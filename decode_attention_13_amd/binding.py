@@ -25,6 +25,7 @@ FP8_CODES = {"f16_kv_e4m3": 3, "bf16_kv_e4m3": 4}
 FP8_CACHE_DTYPES = (torch.float8_e4m3fn, torch.uint8)  # uint8 = raw E4M3 codes
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "kernel": 1, "fused": 2}
+LAUNCHES = {"auto": 0, "grid": 1, "persistent": 2}
 WS_COUNTER_BYTES = 16384  # zeroed head block of every workspace (include/fd.h)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # static scratch of fd_paged_decode_noalloc (include/fd.h)
 HEAD_DIM = 128
@@ -34,7 +35,8 @@ CHUNK_QUANTUM = 64
 class FdOptions(ctypes.Structure):
     _fields_ = [("force_num_splits", ctypes.c_int), ("force_chunk", ctypes.c_int), ("force_kernel", ctypes.c_int),
                 ("debug_checks", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
-                ("split_end_event", ctypes.c_void_p), ("force_merge", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("split_end_event", ctypes.c_void_p), ("force_merge", ctypes.c_int),
+                ("force_launch", ctypes.c_int)]
 
 
 class FdPlan(ctypes.Structure):
@@ -42,11 +44,12 @@ class FdPlan(ctypes.Structure):
                 ("num_splits", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("grid_z", ctypes.c_int), ("threads", ctypes.c_int), ("merge", ctypes.c_int),
                 ("kv_heads_per_group", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t),
-                ("ws_lse_offset", ctypes.c_size_t), ("work_list", ctypes.c_int), ("reserved2", ctypes.c_int),
-                ("ws_err_offset", ctypes.c_size_t), ("ws_o_offset", ctypes.c_size_t)]
+                ("ws_lse_offset", ctypes.c_size_t), ("work_list", ctypes.c_int), ("persistent", ctypes.c_int),
+                ("ws_err_offset", ctypes.c_size_t), ("ws_o_offset", ctypes.c_size_t), ("head_slices", ctypes.c_int),
+                ("reserved3", ctypes.c_int)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved2"}
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved3"}
 
 
 class FdError(RuntimeError):
@@ -128,19 +131,22 @@ def _check(status: int) -> None:
 
 def options(force_num_splits: int = 0, force_chunk: int = 0, kernel: str | int = "auto",
             split_begin_event=None, split_end_event=None, debug_checks: bool | int = False,
-            merge: str | int = "auto") -> FdOptions:
+            merge: str | int = "auto", launch: str | int = "auto") -> FdOptions:
     """An ``fd_options`` block; events are ``torch.cuda.Event`` objects (or raw handles).
     ``debug_checks``: paged calls check the block table and lengths on the device and
     raise ``FdError`` (FD_ERR_BAD_DATA) on an out-of-range value (the call synchronises).
-    ``merge``: "kernel" (a merge kernel), "fused" (the last workgroups merge) or "auto"."""
+    ``merge``: "kernel" (a merge kernel), "fused" (the last workgroups merge) or "auto".
+    ``launch`` (paged calls): "grid" (a workgroup per item), "persistent" (a workgroup per
+    resident slot claiming items) or "auto"."""
     def handle(ev):
         if ev is None:
             return None
         return ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     mg = MERGES[merge] if isinstance(merge, str) else int(merge)
+    ln = LAUNCHES[launch] if isinstance(launch, str) else int(launch)
     return FdOptions(int(force_num_splits), int(force_chunk), k, int(debug_checks), handle(split_begin_event),
-                     handle(split_end_event), mg, 0)
+                     handle(split_end_event), mg, ln)
 
 
 def _opt_ptr(opt):

@@ -133,7 +133,8 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
             return fail(FD_ERR_INVALID_ARG, "fd_options.debug_checks must be 0 or 1 (got %d)", opt->debug_checks);
         if (opt->force_merge < FD_MERGE_AUTO || opt->force_merge > FD_MERGE_FUSED)
             return fail(FD_ERR_INVALID_ARG, "unknown force_merge %d", opt->force_merge);
-        if (opt->reserved != 0) return fail(FD_ERR_INVALID_ARG, "fd_options.reserved must be 0");
+        if (opt->force_launch < FD_LAUNCH_AUTO || opt->force_launch > FD_LAUNCH_PERSISTENT)
+            return fail(FD_ERR_INVALID_ARG, "unknown force_launch %d", opt->force_launch);
     }
     return FD_OK;
 }
@@ -241,6 +242,28 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         p->grid_y = (int)std::min((long long)B + total / chunk, (long long)B * splits);
         p->grid_z = 1;
     }
+    p->head_slices = (int)slices;
+    // Persistent paged launch: when the items would take more than one round of
+    // resident workgroups, one workgroup per slot claims them instead (see
+    // paged_items in fd_device.h). With one workgroup per item, slots emptied by
+    // short items waited microseconds for the dispatcher and the XCDs, which get
+    // workgroups round-robin, finished up to 20% apart on equal work.
+    if (page_size > 0) {
+        const int forced_launch = opt ? opt->force_launch : FD_LAUNCH_AUTO;
+        const long long slots = (long long)num_cus * kPagedSlotsPerCu;
+        const long long items = p->work_list ? (long long)p->grid_y : (long long)B * splits;
+        const bool can = B <= fd::kMaxListSeqs;
+        if (forced_launch == FD_LAUNCH_PERSISTENT && !can)
+            return fail(FD_ERR_UNSUPPORTED, "a persistent launch numbers at most %d sequences", fd::kMaxListSeqs);
+        const bool want = forced_launch == FD_LAUNCH_PERSISTENT ||
+                          (forced_launch == FD_LAUNCH_AUTO && can && items * slices > slots);
+        if (want) {
+            p->persistent = 1;
+            p->grid_x = (int)std::min(slots, items * slices);
+            p->grid_y = 1;
+            p->grid_z = 1;
+        }
+    }
     // Merge of the partials. A fused launch needs a counter per (sequence, head
     // slice) in the workspace's head block and merges at most kFusedMaxSplits
     // splits in one workgroup; a work-list launch keeps the merge kernel (the
@@ -251,9 +274,9 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     // last workgroup) costs about 2.4 us on every workgroup's critical path,
     // while the merge kernel after the split kernel adds only 0.4 us to a step.
     const int forced_merge = opt ? opt->force_merge : FD_MERGE_AUTO;
-    const bool fusable = splits <= fd::kFusedMaxSplits && (long long)B * slices <= fd::kWsCounters &&
+    const bool fusable = splits <= fd::kFusedMaxSplits && (long long)B * slices <= fd::kFusedCounters &&
                          gt * hp <= fd::kFusedMaxHeads && (long long)gt * hp * splits <= fd::kFusedMaxRows &&
-                         !p->work_list;
+                         (!p->work_list || p->persistent);
     if (splits <= 1) {
         p->merge = 0;
     } else if (forced_merge == FD_MERGE_FUSED) {
@@ -272,6 +295,9 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         p->ws_o_offset = FD_WS_COUNTER_BYTES;
         p->ws_lse_offset = p->ws_o_offset + (o_bytes + 255) / 256 * 256;
         p->workspace_bytes = p->ws_lse_offset + rows * sizeof(float);
+    } else if (p->persistent) {
+        p->ws_o_offset = FD_WS_COUNTER_BYTES;
+        p->workspace_bytes = FD_WS_COUNTER_BYTES;  // the claim counters
     }
     // Debug record of a paged call: four ints after the partials.
     if (page_size > 0 && opt && opt->debug_checks) {
@@ -333,7 +359,9 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         a.ws_lse = nullptr;
     }
     a.fused = plan.merge == FD_MERGE_FUSED ? 1 : 0;
-    a.counters = a.fused ? reinterpret_cast<unsigned *>(ws) : nullptr;
+    a.persistent = plan.persistent;
+    a.slices = plan.head_slices;
+    a.counters = plan.workspace_bytes > 0 ? reinterpret_cast<unsigned *>(ws) : nullptr;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
     a.B = B;
@@ -346,10 +374,11 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
     a.heads_per_wg = plan.heads_per_group;
     // 16-token blocks stay inside one page when pages hold at least 16 tokens.
     const int mode = !paged ? fd::kContig : ((1 << a.page_shift) >= 16 ? fd::kPagedBlock : fd::kPagedRow);
+    const bool persist = plan.persistent != 0;
     hipError_t e = plan.kernel == FD_KERNEL_MFMA
-                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, shape, a, stream, ev0, ev1)
-                       : fd::launch_split_valu(dtype, plan.heads_per_group, plan.kv_heads_per_group, mode, shape, a,
-                                               stream, ev0, ev1);
+                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, persist, shape, a, stream, ev0, ev1)
+                       : fd::launch_split_valu(dtype, plan.heads_per_group, plan.kv_heads_per_group, mode, persist,
+                                               shape, a, stream, ev0, ev1);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
     if (plan.merge == FD_MERGE_KERNEL) {
         m.ws_o = a.ws_o;

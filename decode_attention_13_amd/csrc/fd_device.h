@@ -97,6 +97,17 @@ __device__ __forceinline__ float wave_sum(float x) { return pair_sum<32>(pair_su
 // constant rather than blockDim, which would cost a late kernel-argument load.
 constexpr int kSplitThreads = 256;
 
+// ---------------------------------------------------------------- thread index of an item
+// threadIdx.x as a value the optimizer cannot see through. A persistent
+// workgroup runs its items in a loop; offsets derived from this value are then
+// recomputed for every item instead of being hoisted out of the loop, where they
+// would all stay live and push the kernel into register spills.
+__device__ __forceinline__ int item_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // ---------------------------------------------------------------- kernel arguments
 // Marks kernel-argument values as used at this point (an empty asm reading them
 // from scalar registers). Called at kernel entry, it makes the compiler fetch
@@ -411,7 +422,7 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
         // a split spans at most 2*chunk - 1 tokens (the last one takes the remainder)
         const int last = min((t_begin + 2 * a.chunk - 2) >> a.page_shift, a.max_blocks - 1);
         const int32_t *row = a.block_table + (size_t)b * a.max_blocks + first;
-        for (int i = threadIdx.x; i <= last - first; i += kSplitThreads)
+        for (int i = item_tid(); i <= last - first; i += kSplitThreads)
             s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
         __syncthreads();
         *page_first = first;
@@ -437,14 +448,14 @@ __device__ __forceinline__ void report_bad(int *err, int kind, int b, int index,
 // tokens [t_begin, t_end) (t_end <= t_begin when the split is empty); not_last
 // is 0 for the workgroup that owns the sequence's last split.
 __device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int t_begin, int t_end, int not_last) {
-    if (!not_last && threadIdx.x == 0) {
+    if (!not_last && item_tid() == 0) {
         const int L_raw = a.seq_lens[b];
         if (L_raw < 0 || L_raw > a.max_len) report_bad(a.err, kBadSeqLen, b, 0, L_raw);
     }
     if (t_end <= t_begin) return;
     const int first = t_begin >> a.page_shift, last = (t_end - 1) >> a.page_shift;
     const int32_t *row = a.block_table + (size_t)b * a.max_blocks;
-    for (int i = first + (int)threadIdx.x; i <= last; i += kSplitThreads) {
+    for (int i = first + (int)item_tid(); i <= last; i += kSplitThreads) {
         const int page = row[i];
         if (page < 0 || page >= a.num_pages) report_bad(a.err, kBadTableEntry, b, i, page);
     }
@@ -591,6 +602,71 @@ __device__ __forceinline__ bool paged_item(const SplitArgs &a, int *s_start, int
     return true;
 }
 
+// ---------------------------------------------------------------- paged item loop
+// The items of a paged workgroup, each handed to item(args, slice, b, split,
+// not_last). One item per workgroup (paged_item) unless the launch is persistent
+// (a separate kernel instantiation, PERSIST): then grid
+// x is one workgroup per resident slot, and each numbers the items once (the
+// work list) and claims them in item order, largest first, from a counter at the
+// end of the workspace's counter block: claim q is head slice q % slices of list
+// item q / slices. The next claim is issued before the current item is streamed,
+// so its round trip is hidden; no workgroup ever waits for another, and a
+// workgroup that starts late simply claims less. A slot never idles waiting for
+// the dispatcher, and an XCD that streams slower takes fewer items. When the
+// claims run out each workgroup counts itself out on the next counter, and the
+// last one to leave sets both back to zero for the next call. Every thread of
+// the workgroup must call this (it holds barriers).
+// The kernel arguments as read back from an LDS copy for every item: the
+// compiler barrier before the read keeps the optimizer from hoisting anything
+// derived from them out of the item loop, and readfirstlane returns them to
+// scalar registers.
+__device__ __forceinline__ SplitArgs reload_args(const SplitArgs *s_args) {
+    asm volatile("" ::: "memory");
+    SplitArgs r;
+    const int *src = reinterpret_cast<const int *>(s_args);
+    int *dst = reinterpret_cast<int *>(&r);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(SplitArgs) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    return r;
+}
+
+template <typename T, bool PERSIST, typename ItemFn>
+__device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
+    __shared__ int s_start[kMaxListSeqs + 1];
+    __shared__ int s_wave[kSplitThreads / 64];
+    if constexpr (!PERSIST) {
+        int b, split, not_last = 0;
+        if (paged_item<T>(a, s_start, s_wave, b, split, not_last)) item(a, blockIdx.x, b, split, not_last);
+    } else {
+        __shared__ int s_claim;
+        __shared__ SplitArgs s_args;
+        unsigned *const claims = a.counters + kQueueCounter;
+        if (threadIdx.x == 0) s_args = a;
+        const int total = (a.B + build_work_list(a, s_start, s_wave)) * a.slices;
+        int claim = 0;  // thread 0: the claim in flight
+        if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
+        for (;;) {
+            if (threadIdx.x == 0) s_claim = claim;
+            __syncthreads();  // also ends every use of LDS by the previous item
+            const int q = s_claim;
+            __syncthreads();  // s_claim read by all before thread 0 writes the next one
+            if (q >= total) break;
+            if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
+            const int u = q / a.slices;
+            int b, split;
+            work_list_item(s_start, a.B, u, b, split);
+            item(reload_args(&s_args), q - u * a.slices, b, split, 0);
+        }
+        if (threadIdx.x == 0) {
+            const unsigned gone = atomicAdd(claims + 1, 1u) + 1u;
+            if (gone == gridDim.x) {  // every other workgroup has made its last claim
+                __hip_atomic_store(claims, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(claims + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- split epilogue
 // Partials read by another workgroup of the same launch (fused merge) are
 // written and read as device-scope relaxed atomics: on gfx950 these are plain
@@ -628,7 +704,7 @@ __device__ __forceinline__ void fused_merge_rows(const SplitArgs &a, int b, int 
         float lse[kPer][NS], x[kPer][NS];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
-            const int i = min(i0 + e * kSplitThreads + (int)threadIdx.x, nh * kHeadDim - 1);
+            const int i = min(i0 + e * kSplitThreads + (int)item_tid(), nh * kHeadDim - 1);
             const int hh = i / kHeadDim;
             const int d = i - hh * kHeadDim;
             const float *lrow = a.ws_lse + row0 + (size_t)hh * a.num_splits;
@@ -642,7 +718,7 @@ __device__ __forceinline__ void fused_merge_rows(const SplitArgs &a, int b, int 
         }
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
-            const int i = i0 + e * kSplitThreads + (int)threadIdx.x;
+            const int i = i0 + e * kSplitThreads + (int)item_tid();
             if (i >= nh * kHeadDim) break;
             const int hh = i / kHeadDim;
             const int d = i - hh * kHeadDim;
@@ -667,12 +743,12 @@ __device__ __forceinline__ void fused_merge_rows(const SplitArgs &a, int b, int 
 }
 
 template <typename T>
-__device__ void fused_merge_tail(const SplitArgs &a, int b, int h0, int nh, int n_b) {
+__device__ void fused_merge_tail(const SplitArgs &a, int slice, int b, int h0, int nh, int n_b) {
     __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's partial stores are done
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned *ctr = a.counters + (size_t)b * gridDim.x + blockIdx.x;
+    if (item_tid() == 0) {
+        unsigned *ctr = a.counters + (size_t)b * a.slices + slice;
         const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev + 1u == (unsigned)n_b;
         if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -694,9 +770,10 @@ __device__ void fused_merge_tail(const SplitArgs &a, int b, int h0, int nh, int 
 // workspace, for the merge kernel or (fused launch) for the last workgroup of
 // the sequence's head slice.
 template <typename T, typename ValueFn>
-__device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int split, int n_b, ValueFn value) {
+__device__ void finish_split(const SplitArgs &a, int slice, int b, int h0, int nh, int split, int n_b,
+                             ValueFn value) {
     const bool direct = n_b == 1;
-    for (int i = threadIdx.x; i < nh * kHeadDim; i += kSplitThreads) {
+    for (int i = item_tid(); i < nh * kHeadDim; i += kSplitThreads) {
         const int hh = i / kHeadDim;
         const int d = i - hh * kHeadDim;
         float lse;
@@ -714,7 +791,7 @@ __device__ void finish_split(const SplitArgs &a, int b, int h0, int nh, int spli
             if (d == 0) a.ws_lse[row] = lse;
         }
     }
-    if (!direct && a.fused) fused_merge_tail<T>(a, b, h0, nh, n_b);
+    if (!direct && a.fused) fused_merge_tail<T>(a, slice, b, h0, nh, n_b);
 }
 
 }  // namespace fd

@@ -148,20 +148,22 @@ struct KvFrag<T, fp8e4m3> {
 };
 
 template <typename T, typename KV, int MODE>
-__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b, const int split, const int not_last) {
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int slice, const int b, const int split,
+                                                const int not_last) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
     using F = KvFrag<T, KV>;
     constexpr int KR = F::kKRegs;
     using E = Elem<T>;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = item_tid();
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int g = lane >> 4;   // 16-lane group
     const int c = lane & 15;   // row/column inside the 16x16 tile
     const int G = a.G;
-    const int slices = G / a.heads_per_wg;
-    const int kvh = blockIdx.x / slices;
-    const int h0 = kvh * G + (blockIdx.x - kvh * slices) * a.heads_per_wg;
+    const int per_kv = G / a.heads_per_wg;
+    const int kvh = slice / per_kv;
+    const int h0 = kvh * G + (slice - kvh * per_kv) * a.heads_per_wg;
     const int nh = a.heads_per_wg;  // heads of this workgroup (<= 16)
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
@@ -180,7 +182,7 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
     if (split >= n_b - not_last) {  // uniform over the workgroup
         if (split == 0 && !not_last) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
-            for (int i = threadIdx.x; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
+            for (int i = tid; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
         return;
     }
@@ -380,7 +382,7 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
         }
     }
     __syncthreads();
-    finish_split<T>(a, b, h0, nh, split, n_b, [&](int hh, int d, float &lse) {
+    finish_split<T>(a, slice, b, h0, nh, split, n_b, [&](int hh, int d, float &lse) {
         float Mx = s_m[0][hh];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][hh]);
@@ -397,51 +399,55 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int b,
     });
 }
 
-// One workgroup per (head slice, split, sequence). Paged batches take their
+// Contiguous: one workgroup per (head slice, split). Paged batches take their
 // (sequence, split) items largest first, the last split of every sequence
-// before the others (paged_item); with a work list (a batch much shorter than
-// its longest sequence) grid y numbers only items that exist, so no workgroup
-// is launched only to find its split empty.
-template <typename T, typename KV, int MODE>
+// before the others, one per workgroup or, in a persistent launch, claimed by
+// one workgroup per resident slot (paged_items).
+template <typename T, typename KV, int MODE, bool PERSIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
     pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
-    int b = blockIdx.z, split = blockIdx.y, not_last = 0;
-    if constexpr (MODE != kContig) {
-        __shared__ int s_start[kMaxListSeqs + 1];
-        __shared__ int s_wave[kSplitThreads / 64];
-        if (!paged_item<T>(a, s_start, s_wave, b, split, not_last)) return;
+    if constexpr (MODE == kContig) {
+        split_mfma_item<T, KV, MODE>(a, blockIdx.x, 0, blockIdx.y, 0);
+    } else {
+        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split, int not_last) {
+            split_mfma_item<T, KV, MODE>(ai, x, b, split, not_last);
+        });
     }
-    split_mfma_item<T, KV, MODE>(a, b, split, not_last);
 }
 
-template <typename T, typename KV, int MODE>
+template <typename T, typename KV, int MODE, bool PERSIST>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, KV, MODE>), s, args, st, e0, e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, KV, MODE, PERSIST>), s, args, st, e0,
+                        e1);
 }
 
 template <typename T, typename KV>
-hipError_t launch_mode(int mode, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
+hipError_t launch_mode(int mode, bool persist, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_one<T, KV, kContig>(s, a, st, e0, e1);
-        case kPagedBlock: return launch_one<T, KV, kPagedBlock>(s, a, st, e0, e1);
-        case kPagedRow: return launch_one<T, KV, kPagedRow>(s, a, st, e0, e1);
+        case kContig: return launch_one<T, KV, kContig, false>(s, a, st, e0, e1);
+        case kPagedBlock:
+            return persist ? launch_one<T, KV, kPagedBlock, true>(s, a, st, e0, e1)
+                           : launch_one<T, KV, kPagedBlock, false>(s, a, st, e0, e1);
+        case kPagedRow:
+            return persist ? launch_one<T, KV, kPagedRow, true>(s, a, st, e0, e1)
+                           : launch_one<T, KV, kPagedRow, false>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, const LaunchShape &s, const SplitArgs &a,
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, bool persist, const LaunchShape &s, const SplitArgs &a,
                              hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if (gt < 1 || gt > kMaxHeads) return hipErrorInvalidValue;
     switch (dtype) {
-        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, s, a, st, e0, e1);
-        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, s, a, st, e0, e1);
-        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

@@ -24,6 +24,8 @@
 // are merged once at the end (lane swaps across rows inside a wave, LDS
 // across waves) and written as a normalised partial plus its natural-log lse, or,
 // when one split covers the sequence, as the final output.
+#include <type_traits>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -43,7 +45,8 @@ constexpr int kWaves = kThreads / 64;
 // (measured with a plain read kernel on the 32-head layout: 12.7 against 10.8 us
 // for 64 MB).
 template <typename T, typename KV, int GT, int HP, int MODE>
-__device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b, const int split, const int not_last) {
+__device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int slice, const int b, const int split,
+                                                const int not_last) {
     static_assert(HP == 1 || GT == 1, "packed KV heads are for MHA");
     constexpr bool PAGED = MODE != kContig;
     using E = Elem<T>;
@@ -55,20 +58,21 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b,
     constexpr int kTok = 4 / HP;              // tokens per load instruction
     constexpr int kWaveTile = kRows * kTok;   // tokens per wave tile
     constexpr int NH = HP * GT;               // query heads of the workgroup
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = item_tid();
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int grp = lane >> 4;
     const int c = lane & 15;
     const int hs = grp % HP;  // this group's KV head within the workgroup
     const int ts = grp / HP;  // this group's token within a load instruction
     int kvh, h0;
     if constexpr (HP > 1) {  // G = 1: query head = KV head
-        kvh = blockIdx.x * HP;
+        kvh = slice * HP;
         h0 = kvh;
     } else {
-        const int slices = a.G / GT;
-        kvh = blockIdx.x / slices;
-        h0 = kvh * a.G + (blockIdx.x - kvh * slices) * GT;
+        const int per_kv = a.G / GT;
+        kvh = slice / per_kv;
+        h0 = kvh * a.G + (slice - kvh * per_kv) * GT;
     }
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
@@ -87,7 +91,7 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b,
     if (split >= n_b - not_last) {  // uniform over the workgroup
         if (split == 0 && !not_last) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
-            for (int i = threadIdx.x; i < NH * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
+            for (int i = tid; i < NH * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
         return;
     }
@@ -281,7 +285,7 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b,
     __syncthreads();
 
     // Merge the waves, then store the split (or the merged output).
-    finish_split<T>(a, b, h0, NH, split, n_b, [&](int gi, int d, float &lse) {
+    finish_split<T>(a, slice, b, h0, NH, split, n_b, [&](int gi, int d, float &lse) {
         float M = s_m[0][gi];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gi]);
@@ -298,67 +302,73 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int b,
     });
 }
 
-// One workgroup per (head slice, split, sequence). Paged batches take their
+// Contiguous: one workgroup per (head slice, split). Paged batches take their
 // (sequence, split) items largest first, the last split of every sequence
-// before the others (paged_item); with a work list (a batch much shorter than
-// its longest sequence) grid y numbers only items that exist, so no workgroup
-// is launched only to find its split empty.
-template <typename T, typename KV, int GT, int HP, int MODE>
+// before the others, one per workgroup or, in a persistent launch, claimed by
+// one workgroup per resident slot (paged_items).
+template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST>
 __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
-    int b = blockIdx.z, split = blockIdx.y, not_last = 0;
-    if constexpr (MODE != kContig) {
-        __shared__ int s_start[kMaxListSeqs + 1];
-        __shared__ int s_wave[kSplitThreads / 64];
-        if (!paged_item<T>(a, s_start, s_wave, b, split, not_last)) return;
+    if constexpr (MODE == kContig) {
+        split_valu_item<T, KV, GT, HP, MODE>(a, blockIdx.x, 0, blockIdx.y, 0);
+    } else {
+        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split, int not_last) {
+            split_valu_item<T, KV, GT, HP, MODE>(ai, x, b, split, not_last);
+        });
     }
-    split_valu_item<T, KV, GT, HP, MODE>(a, b, split, not_last);
 }
 
-template <typename T, typename KV, int GT, int HP, int MODE>
+template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, KV, GT, HP, MODE>), s, args, st, e0,
-                        e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, KV, GT, HP, MODE, PERSIST>), s, args, st,
+                        e0, e1);
 }
 
-template <typename T, typename KV, int MODE>
+template <typename T, typename KV, int MODE, bool PERSIST>
 hipError_t launch_gt(int gt, int hp, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
                      hipEvent_t e1) {
-    if (hp == 2 && gt == 1) return launch_one<T, KV, 1, 2, MODE>(s, a, st, e0, e1);
-    if (hp == 4 && gt == 1) return launch_one<T, KV, 1, 4, MODE>(s, a, st, e0, e1);
+    if (hp == 2 && gt == 1) return launch_one<T, KV, 1, 2, MODE, PERSIST>(s, a, st, e0, e1);
+    if (hp == 4 && gt == 1) return launch_one<T, KV, 1, 4, MODE, PERSIST>(s, a, st, e0, e1);
     if (hp != 1) return hipErrorInvalidValue;
     switch (gt) {
-        case 1: return launch_one<T, KV, 1, 1, MODE>(s, a, st, e0, e1);
-        case 2: return launch_one<T, KV, 2, 1, MODE>(s, a, st, e0, e1);
-        case 4: return launch_one<T, KV, 4, 1, MODE>(s, a, st, e0, e1);
-        case 8: return launch_one<T, KV, 8, 1, MODE>(s, a, st, e0, e1);
+        case 1: return launch_one<T, KV, 1, 1, MODE, PERSIST>(s, a, st, e0, e1);
+        case 2: return launch_one<T, KV, 2, 1, MODE, PERSIST>(s, a, st, e0, e1);
+        case 4: return launch_one<T, KV, 4, 1, MODE, PERSIST>(s, a, st, e0, e1);
+        case 8:
+            // fp32 rows stop at 4 heads per workgroup (the planner never asks for 8)
+            if constexpr (std::is_same<T, float>::value) return hipErrorInvalidValue;
+            else return launch_one<T, KV, 8, 1, MODE, PERSIST>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, typename KV>
-hipError_t launch_mode(int mode, int gt, int hp, const LaunchShape &s, const SplitArgs &a, hipStream_t st,
-                       hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_mode(int mode, bool persist, int gt, int hp, const LaunchShape &s, const SplitArgs &a,
+                       hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (mode) {
-        case kContig: return launch_gt<T, KV, kContig>(gt, hp, s, a, st, e0, e1);
-        case kPagedBlock: return launch_gt<T, KV, kPagedBlock>(gt, hp, s, a, st, e0, e1);
-        case kPagedRow: return launch_gt<T, KV, kPagedRow>(gt, hp, s, a, st, e0, e1);
+        case kContig: return launch_gt<T, KV, kContig, false>(gt, hp, s, a, st, e0, e1);
+        case kPagedBlock:
+            return persist ? launch_gt<T, KV, kPagedBlock, true>(gt, hp, s, a, st, e0, e1)
+                           : launch_gt<T, KV, kPagedBlock, false>(gt, hp, s, a, st, e0, e1);
+        case kPagedRow:
+            return persist ? launch_gt<T, KV, kPagedRow, true>(gt, hp, s, a, st, e0, e1)
+                           : launch_gt<T, KV, kPagedRow, false>(gt, hp, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, const LaunchShape &s, const SplitArgs &a,
-                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, bool persist, const LaunchShape &s,
+                             const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (dtype) {
-        case FD_DTYPE_F32: return launch_mode<float, float>(mode, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F32: return launch_mode<float, float>(mode, persist, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, gt, hp, s, a, st, e0, e1);
     }
     return hipErrorInvalidValue;
 }

@@ -77,6 +77,12 @@ enum {
 };
 
 enum {
+    FD_LAUNCH_AUTO = 0,       /* planner's choice */
+    FD_LAUNCH_GRID = 1,       /* paged: one workgroup per (head slice, split, sequence) */
+    FD_LAUNCH_PERSISTENT = 2  /* paged: one workgroup per resident slot, each claiming items in turn */
+};
+
+enum {
     FD_KERNEL_AUTO = 0, /* planner's choice */
     FD_KERNEL_VALU = 1, /* vector-ALU split kernel (any head group, every dtype) */
     FD_KERNEL_MFMA = 2  /* matrix-core split kernel (f16/bf16, H/Hkv <= 16 or a multiple of 16) */
@@ -106,7 +112,8 @@ typedef struct fd_options {
                                 (both set by the dispatch itself: hipExtLaunchKernel) */
     int force_merge;         /* FD_MERGE_*: how the partials of a multi-split plan are merged;
                                 FD_MERGE_FUSED where the plan cannot fuse is FD_ERR_UNSUPPORTED */
-    int reserved;            /* must be 0 */
+    int force_launch;        /* FD_LAUNCH_*: paged calls only (contiguous ones launch a grid);
+                                FD_LAUNCH_PERSISTENT needs B <= 1024, else FD_ERR_UNSUPPORTED */
 } fd_options;
 
 /* What a call with the same arguments would launch. */
@@ -115,8 +122,8 @@ typedef struct fd_plan {
     int heads_per_group; /* query heads of one KV head that one workgroup computes (they share its rows) */
     int chunk;           /* split stride: every split but a sequence's last holds this many tokens */
     int num_splits;      /* splits of the longest sequence, max(1, floor(max_len / chunk)) = grid y */
-    int grid_x, grid_y, grid_z; /* split kernel grid: (head slices = Hkv / kv_heads_per_group *
-                                   (H / Hkv) / heads_per_group, splits, sequences); see work_list */
+    int grid_x, grid_y, grid_z; /* split kernel grid: (head_slices, splits, sequences); see work_list
+                                   and persistent */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 0: one split per sequence, o written directly; 1 (FD_MERGE_KERNEL): partials
                             go to the workspace and a merge kernel runs; 2 (FD_MERGE_FUSED): one launch, the
@@ -129,12 +136,21 @@ typedef struct fd_plan {
                                split of every sequence first, then the others sequence by sequence),
                                grid_z = 1, one split per workgroup; chosen when the (splits x
                                sequences) grid would be mostly empty splits and total_kv is known */
-    int reserved2;
+    int persistent;         /* 1 (paged only): grid_x = one workgroup per resident slot (two per compute
+                               unit), grid_y = grid_z = 1; every workgroup numbers the items as the work
+                               list does and claims them, largest first, from a counter in the
+                               workspace's counter block until none is left. Chosen when the item grid
+                               would take more than one round of resident workgroups (B <= 1024). The
+                               split stride, the splits and so the results are those of the grid form;
+                               total_kv only sizes the splits (every item is processed). */
     size_t ws_err_offset;   /* paged plans with debug_checks: byte offset of the 16-byte error
                                record (int32 kind, sequence, table index or 0, offending value;
                                kind 1 = table entry, 2 = sequence length) inside the workspace,
                                which workspace_bytes then includes; 0 otherwise */
     size_t ws_o_offset;     /* byte offset of ws_o inside the workspace (FD_WS_COUNTER_BYTES) */
+    int head_slices;        /* Hkv / kv_heads_per_group * (H / Hkv) / heads_per_group: workgroup-sized
+                               slices of the heads of one sequence */
+    int reserved3;
 } fd_plan;
 
 /*
@@ -142,10 +158,14 @@ typedef struct fd_plan {
  * workspace serves calls of any plan):
  *   counters [FD_WS_COUNTER_BYTES / 4] uint32 at byte 0: a fused launch counts
  *                                the finished splits of each (sequence, head
- *                                slice) here. They must be ZERO before the
- *                                workspace is first used (e.g. hipMemset once
- *                                after allocating it); every completed call
- *                                leaves them zero.
+ *                                slice) from the start of the block, a
+ *                                persistent launch its claims in the last two
+ *                                words. They must be ZERO before the workspace
+ *                                is first used (e.g. hipMemset once after
+ *                                allocating it); every completed call leaves
+ *                                them zero. A persistent plan needs this block
+ *                                even when it has one split (workspace_bytes
+ *                                >= FD_WS_COUNTER_BYTES).
  *   ws_o  [B, H, num_splits, D]  fp32, normalised output of each split, at
  *                                byte offset ws_o_offset
  *   ws_lse[B, H, num_splits]     fp32, natural-log log-sum-exp of each split's
@@ -238,9 +258,10 @@ fd_status fd_decode(const void *q, const void *k, const void *v, void *o,
  *   total_kv     host-side sum of L_b (each clamped to max_seq_len and to the
  *                table's reach) if known (> 0), else <= 0. It sizes the splits
  *                and, for a batch far shorter than its longest sequence, the
- *                work-list grid (fd_plan.work_list); a value below the true sum
- *                may leave splits unlaunched, whose outputs are then NaN. A
- *                larger value only costs idle workgroups.
+ *                work-list grid (fd_plan.work_list); in a work-list grid a value
+ *                below the true sum leaves splits unlaunched, whose outputs are
+ *                then NaN (a persistent launch processes every split whatever
+ *                the value). A larger value only costs idle workgroups.
  *   Other arguments as in fd_decode.
  */
 fd_status fd_paged_decode(const void *q, const void *k_cache, const void *v_cache,

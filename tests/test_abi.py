@@ -48,19 +48,24 @@ def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
     assert p["chunk"] % 16 == 0 and p["chunk"] >= 16  # whole 16-token addressing blocks
     # floor: the last split of a sequence also takes the remainder
     assert p["num_splits"] == max(1, max_len // p["chunk"])
-    if p["work_list"]:  # splits that hold tokens, numbered; at most the full grid
-        assert p["grid_z"] == 1 and 1 <= p["grid_y"] <= B * p["num_splits"]
-    else:
-        assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B
     gt, hp = p["heads_per_group"], p["kv_heads_per_group"]
     assert (H // Hkv) % gt == 0 and Hkv % hp == 0 and (hp == 1 or H == Hkv)
-    assert p["grid_x"] == (Hkv // hp) * (H // Hkv) // gt
+    slices = (Hkv // hp) * (H // Hkv) // gt
+    assert p["head_slices"] == slices
+    if p["persistent"]:  # one workgroup per resident slot (two per CU), claiming items
+        assert p["grid_y"] == 1 and p["grid_z"] == 1 and 1 <= p["grid_x"] <= 2 * 256
+        assert p["workspace_bytes"] >= binding.WS_COUNTER_BYTES and B <= 1024
+    elif p["work_list"]:  # splits that hold tokens, numbered; at most the full grid
+        assert p["grid_z"] == 1 and 1 <= p["grid_y"] <= B * p["num_splits"] and p["grid_x"] == slices
+    else:
+        assert p["grid_y"] == p["num_splits"] and p["grid_z"] == B and p["grid_x"] == slices
     if p["merge"]:
         rows = B * H * p["num_splits"]
         assert p["ws_lse_offset"] >= rows * 128 * 4 and p["ws_lse_offset"] % 256 == 0
         assert p["workspace_bytes"] == p["ws_lse_offset"] + rows * 4
     else:
-        assert p["num_splits"] == 1 and p["workspace_bytes"] == 0
+        assert p["num_splits"] == 1
+        assert p["workspace_bytes"] == (binding.WS_COUNTER_BYTES if p["persistent"] else 0)
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
@@ -101,12 +106,16 @@ def test_plan_work_list_choice():
     # splits, so a known total switches to the numbered work list
     w = WORKLOADS["paged_gqa8_f16_b128_s256-64k"]
     L = w.seq_lens()
-    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
-    assert p["work_list"] == 1 and p["grid_z"] == 1
+    grid = fd.options(launch="grid")
+    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256, grid)
+    assert p["work_list"] == 1 and p["grid_z"] == 1 and p["persistent"] == 0
     assert p["grid_y"] == w.B + int(L.sum()) // p["chunk"]
     assert p["grid_y"] >= sum(max(1, int(x) // p["chunk"]) for x in L)  # every split has a workgroup
+    # by default the same items are claimed by one workgroup per resident slot
+    d = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+    assert d["persistent"] == 1 and d["grid_x"] == 512 and d["chunk"] == p["chunk"]
     # unknown total, contiguous decode, one sequence, uniform lengths: the full grid
-    assert fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256)["work_list"] == 0
+    assert fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256, grid)["work_list"] == 0
     assert fd.decode_plan(32, 32, 131072, "bf16", 256)["work_list"] == 0
     assert fd.paged_plan(1, 32, 8, "bf16", 16, 65536, 65536, 256)["work_list"] == 0
     assert fd.paged_plan(64, 32, 8, "bf16", 16, 8192, 64 * 8192, 256)["work_list"] == 0
@@ -126,7 +135,7 @@ def test_plan_paged_strides_of_the_batches():
             assert (p["chunk"], p["work_list"]) == (chunk, wl), (name, dt, p)
     w = WORKLOADS["paged_gqa8_f16_b128_s256-64k"]
     L = w.seq_lens()
-    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256)
+    p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), 0, 256, fd.options(launch="grid"))
     assert p["work_list"] == 0 and p["grid_z"] == w.B
 
 
@@ -337,3 +346,30 @@ def test_merge_choice():
     assert fd.decode_plan(8, 8, 100, "f32", 256, fd.options(force_num_splits=1))["merge"] == 0
     with pytest.raises(fd.FdError):
         fd.decode_plan(8, 8, 512, "f32", 256, fd.options(merge=3))
+
+
+def test_persistent_launch_choice():
+    """Paged batches whose items would take more than one round of resident workgroups
+    (two per CU) run one workgroup per slot; smaller batches and contiguous decodes
+    keep one workgroup per item; forcing is honoured where possible."""
+    for name in ("paged_gqa4_bf16_b64_s1k-8k", "paged_gqa8_f16_b128_s256-64k"):
+        w = WORKLOADS[name]
+        L = w.seq_lens()
+        args = (w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
+        p = fd.paged_plan(*args)
+        g = fd.paged_plan(*args, fd.options(launch="grid"))
+        assert p["persistent"] == 1 and p["grid_x"] == 512 and g["persistent"] == 0
+        assert p["chunk"] == g["chunk"] and p["num_splits"] == g["num_splits"] and p["merge"] == g["merge"]
+        assert p["workspace_bytes"] == g["workspace_bytes"]
+    small = fd.paged_plan(2, 32, 8, "bf16", 16, 2000, 3000, 256)  # 31 splits x 2 x 8 slices <= 512
+    assert small["persistent"] == 0
+    forced = fd.paged_plan(4, 32, 8, "bf16", 16, 100, 400, 256, fd.options(launch="persistent", force_chunk=128))
+    assert forced["persistent"] == 1 and forced["merge"] == 0
+    assert forced["workspace_bytes"] == binding.WS_COUNTER_BYTES  # the claim counters
+    assert forced["grid_x"] == forced["head_slices"] * 4  # never more workgroups than items
+    assert fd.decode_plan(32, 32, 131072, "bf16", 256)["persistent"] == 0
+    with pytest.raises(fd.FdError) as e:
+        fd.paged_plan(1025, 8, 2, "bf16", 16, 100, 1025 * 100, 256, fd.options(launch="persistent"))
+    assert e.value.name == "FD_ERR_UNSUPPORTED"
+    with pytest.raises(fd.FdError):
+        fd.paged_plan(4, 32, 8, "bf16", 16, 100, 400, 256, fd.options(launch=3))

@@ -281,6 +281,11 @@ def test_paged_workloads(name, device):
         announce(f"{name} run {kernel}")
         o = run_paged(d, device, opt=fd.options(kernel=kernel))
         assert_close(o, ref, w.dtype, f"{name} {kernel}")
+    announce(f"{name} grid launch")
+    auto = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, 16, d["max_seq_len"], d["total_kv"])
+    assert auto["persistent"] == 1
+    og = run_paged(d, device, opt=fd.options(launch="grid"))
+    assert torch.equal(og, run_paged(d, device))  # the same splits claimed or one per workgroup
 
 
 # ------------------------------------------------------------------ invariance and tails
@@ -499,24 +504,31 @@ def _ragged_batch(B, seed, lo=1, hi=6000):
 
 @pytest.mark.parametrize("kernel", ["auto", "valu"])
 def test_work_list_matches_grid(kernel, device):
-    """A batch far shorter than its longest sequence: with total_kv the splits that
-    hold tokens are numbered (work list), without it the full (split, sequence) grid
-    runs. Same splits, same arithmetic: bit-identical outputs, and the oracle agrees."""
+    """A batch far shorter than its longest sequence, three launches of the same
+    splits: numbered items (work list, total_kv given), the full (split, sequence)
+    grid (total_kv unknown), and one workgroup per resident slot claiming the items
+    (persistent). Same splits, same arithmetic: bit-identical outputs, and the oracle
+    agrees."""
     lens, d = _ragged_batch(48, 420)
-    opt = fd.options(force_chunk=256, kernel=kernel)
     total = sum(lens)
-    p_list = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), total, 0, opt)
-    p_grid = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), 0, 0, opt)
-    assert p_list["work_list"] == 1 and p_grid["work_list"] == 0
+    opts = {"list": fd.options(force_chunk=256, kernel=kernel, launch="grid"),
+            "grid": fd.options(force_chunk=256, kernel=kernel, launch="grid"),
+            "persistent": fd.options(force_chunk=256, kernel=kernel)}
+    totals = {"list": total, "grid": 0, "persistent": total}
+    p_list = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), total, 0, opts["list"])
+    p_grid = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), 0, 0, opts["grid"])
+    p_pers = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), total, 0, opts["persistent"])
+    assert p_list["work_list"] == 1 and p_grid["work_list"] == 0 and p_pers["persistent"] == 1
     assert p_list["grid_y"] == 48 + total // 256
     outs = []
-    for tk in (total, 0):
-        announce(f"work list {kernel} total_kv={tk}")
+    for name in ("list", "grid", "persistent"):
+        announce(f"work list {kernel} {name}")
         g = to_dev(d, device)
         outs.append(fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
-                                       scale=d["scale"], max_seq_len=max(lens), total_kv=tk, opt=opt).cpu())
+                                       scale=d["scale"], max_seq_len=max(lens), total_kv=totals[name],
+                                       opt=opts[name]).cpu())
         torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
     assert torch.all(outs[0][3] == 0)
     pairs = _sample_pairs(48, 32, np.array(lens), 6, 421)
     ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
@@ -525,11 +537,12 @@ def test_work_list_matches_grid(kernel, device):
 
 
 def test_work_list_short_total_is_nan(device):
-    """total_kv below the true sum: the splits past the shortened work list have no
-    workgroup, and exactly the sequences that own one come out NaN; every other
-    sequence is bit-identical to the full-grid result."""
+    """total_kv below the true sum, work-list grid: the splits past the shortened work
+    list have no workgroup, and exactly the sequences that own one come out NaN; every
+    other sequence is bit-identical to the full-grid result. A persistent launch
+    numbers the items on the device and gets every sequence right."""
     lens, d = _ragged_batch(48, 430)
-    opt = fd.options(force_chunk=256)
+    opt = fd.options(force_chunk=256, launch="grid")
     short = sum(lens) // 3
     plan = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), short, 0, opt)
     assert plan["work_list"] == 1
@@ -552,6 +565,13 @@ def test_work_list_short_total_is_nan(device):
             assert torch.isnan(outs[0][b].float()).all(), b
         else:
             assert torch.equal(outs[0][b], outs[1][b]), b
+    pers = fd.options(force_chunk=256, launch="persistent")
+    assert fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), short, 0, pers)["persistent"] == 1
+    announce("persistent, short total_kv")
+    o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                           scale=d["scale"], max_seq_len=max(lens), total_kv=short, opt=pers).cpu()
+    torch.cuda.synchronize()
+    assert torch.equal(o, outs[1])
 
 
 def test_workspace_too_small_is_rejected(device):
@@ -656,23 +676,26 @@ def test_paged_long_sequence(device):
 # ------------------------------------------------------------------ paged partials, sweep lengths
 
 
+@pytest.mark.parametrize("launch", ["grid", "persistent"])
 @pytest.mark.parametrize("work_list", [True, False])
 @pytest.mark.parametrize("kernel", ["mfma", "valu"])
-def test_paged_partials(kernel, work_list, device):
+def test_paged_partials(kernel, work_list, launch, device):
     """The paged split kernels alone: ws_o / ws_lse of every split of every (sequence,
     head) of a ragged batch on shuffled pages, against the oracle's paged partials over
     the library's token ranges; with the numbered work list (total_kv given) and with
-    the full grid. The workspace starts NaN-filled, so an unwritten partial shows."""
+    the full grid, and as one workgroup per resident slot claiming the items. The
+    workspace starts NaN-filled, so an unwritten partial shows."""
     lens = [5, 300, 1500, 4000, 2049, 0, 64, 3333]
     B, H, Hkv, chunk = len(lens), 32, 8, 256
     d = inputs.paged_inputs(B, H, Hkv, 128, "bf16", 16, lens, 960)
-    opt = fd.options(force_chunk=chunk, kernel=kernel)
+    opt = fd.options(force_chunk=chunk, kernel=kernel, launch=launch)
     total = sum(lens) if work_list else 0
     plan = fd.paged_plan(B, H, Hkv, "bf16", 16, max(lens), total, 0, opt)
     assert plan["work_list"] == int(work_list) and plan["merge"] == 1 and plan["chunk"] == chunk
+    assert plan["persistent"] == (launch == "persistent")
     ws = poisoned_workspace(plan["workspace_bytes"], device)
     g = to_dev(d, device)
-    announce(f"paged partials {kernel} work_list={work_list}")
+    announce(f"paged partials {kernel} work_list={work_list} {launch}")
     o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
                            scale=d["scale"], max_seq_len=max(lens), total_kv=total, opt=opt, ws=ws)
     torch.cuda.synchronize()
@@ -731,9 +754,10 @@ def test_sweep_length_full_size(S, device):
 # ------------------------------------------------------------------ device-data checks
 
 
+@pytest.mark.parametrize("launch", ["auto", "persistent"])
 @pytest.mark.parametrize("work_list", [True, False])
 @pytest.mark.parametrize("kernel", ["auto", "valu"])
-def test_debug_checks_report_bad_table_and_lengths(kernel, work_list, device):
+def test_debug_checks_report_bad_table_and_lengths(kernel, work_list, launch, device):
     """fd_options.debug_checks: a clean batch gives the same output bit for bit as
     without it; a table entry outside [0, num_pages) inside a sequence's pages, or a
     negative length, comes back as FD_ERR_BAD_DATA naming the sequence and index.
@@ -747,16 +771,17 @@ def test_debug_checks_report_bad_table_and_lengths(kernel, work_list, device):
     total = sum(lens) if work_list else 0
 
     def call(debug, table=None, seq_lens=None):
-        opt = fd.options(force_chunk=256, kernel=kernel, debug_checks=debug)
+        opt = fd.options(force_chunk=256, kernel=kernel, debug_checks=debug, launch=launch)
         o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"] if table is None else table,
                                g["seq_lens"] if seq_lens is None else seq_lens, 16, scale=d["scale"],
                                max_seq_len=max(lens), total_kv=total, opt=opt)
         torch.cuda.synchronize()
         return o.cpu()
 
-    plan = fd.paged_plan(4, 32, 8, "bf16", 16, max(lens), total, 0, fd.options(force_chunk=256, kernel=kernel))
-    assert plan["work_list"] == int(work_list)
-    announce(f"debug checks {kernel} work_list={work_list}: clean")
+    plan = fd.paged_plan(4, 32, 8, "bf16", 16, max(lens), total, 0,
+                         fd.options(force_chunk=256, kernel=kernel, launch=launch))
+    assert plan["work_list"] == int(work_list) and plan["persistent"] == (launch == "persistent")
+    announce(f"debug checks {kernel} work_list={work_list} {launch}: clean")
     clean = call(False)
     assert torch.equal(call(True), clean)
     bad = d["block_table"].clone()
@@ -867,5 +892,16 @@ def test_fused_paged_grid(device):
         assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)
     with pytest.raises(fd.FdError) as e:
         fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), sum(lens), 0,
-                      fd.options(force_chunk=256, merge="fused"))
+                      fd.options(force_chunk=256, merge="fused", launch="grid"))
     assert e.value.name == "FD_ERR_UNSUPPORTED"
+    # a persistent launch processes every item, so its work list can fuse
+    opt = fd.options(force_chunk=256, merge="fused", launch="persistent")
+    plan = fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), sum(lens), 0, opt)
+    assert plan["merge"] == 2 and plan["work_list"] == 1 and plan["persistent"] == 1
+    ws = poisoned_workspace(plan["workspace_bytes"], device)
+    announce("fused paged persistent work list")
+    o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                           scale=d["scale"], max_seq_len=max(lens), total_kv=sum(lens), opt=opt, ws=ws)
+    torch.cuda.synchronize()
+    assert_close(o, ref, "bf16", "fused paged persistent")
+    assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)
