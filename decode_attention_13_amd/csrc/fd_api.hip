@@ -144,9 +144,17 @@ fd_status check_common(int B, int H, int Hkv, int D, fd_dtype dtype, const fd_op
 // When the full (splits x sequences) grid would be more than twice that, the
 // launch holds that many workgroups instead. An understated total_kv leaves
 // items without a workgroup; their outputs become NaN.
+// Splits of a sequence of `len` tokens: ceil(len / chunk) for a paged batch (the
+// last split holds the remainder), max(1, floor(len / chunk)) for a contiguous
+// cache (the last split also takes the remainder); at least one, so that a
+// plan always has a split to hold an empty sequence's zeros.
+long long splits_for(long long len, long long chunk, bool paged) {
+    return paged ? std::max(1LL, (len + chunk - 1) / chunk) : std::max(1LL, len / chunk);
+}
+
 bool uses_work_list(int B, int max_len, long long total, bool total_known, long long chunk) {
     if (!total_known || B <= 1 || B > fd::kMaxListSeqs) return false;
-    const long long splits = std::max(1LL, (long long)max_len / chunk);
+    const long long splits = splits_for(max_len, chunk, true);
     const long long items = (long long)B + total / chunk;
     return (long long)B * splits >= 2 * items;
 }
@@ -199,11 +207,11 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         chunk = pow2_floor(std::max(1LL, work / target));
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
-    // A split spans up to 2*chunk - 1 tokens (the last one takes the remainder),
-    // i.e. up to (2*chunk - 2) / page_size + 2 pages, and its slice of the block
-    // table must fit the LDS stage of kMaxSplitPages entries.
+    // A paged split spans at most chunk tokens, i.e. at most (chunk - 1) / page_size
+    // + 2 pages, and its slice of the block table must fit the LDS stage of
+    // kMaxSplitPages entries.
     const long long page_cap =
-        page_size > 0 ? ((long long)(fd::kMaxSplitPages - 2) * page_size + 2) / 2 : (long long)1 << 40;
+        page_size > 0 ? (long long)(fd::kMaxSplitPages - 2) * page_size + 1 : (long long)1 << 40;
     if (page_size > 0) {
         const long long cap = page_cap / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
         if (chunk > cap) {
@@ -213,14 +221,14 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
             chunk = std::max<long long>(cap, FD_CHUNK_QUANTUM);
         }
     }
-    // max(1, floor(max_len / chunk)) splits: the last one of a sequence takes the remainder.
-    long long splits = std::max(1LL, (long long)max_len / chunk);
+    const bool paged = page_size > 0;
+    long long splits = splits_for(max_len, chunk, paged);
     if (splits > kMaxSplits) {
         chunk = ((long long)max_len + kMaxSplits - 1) / kMaxSplits;
         chunk = (chunk + FD_CHUNK_QUANTUM - 1) / FD_CHUNK_QUANTUM * FD_CHUNK_QUANTUM;
         if (chunk > page_cap)
             return fail(FD_ERR_UNSUPPORTED, "sequence of %d tokens needs more than %d splits", max_len, kMaxSplits);
-        splits = std::max(1LL, (long long)max_len / chunk);
+        splits = splits_for(max_len, chunk, paged);
     }
 
     std::memset(p, 0, sizeof(*p));
@@ -274,15 +282,16 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
     // last workgroup) costs about 2.4 us on every workgroup's critical path,
     // while the merge kernel after the split kernel adds only 0.4 us to a step.
     const int forced_merge = opt ? opt->force_merge : FD_MERGE_AUTO;
-    const bool fusable = splits <= fd::kFusedMaxSplits && (long long)B * slices <= fd::kFusedCounters &&
-                         gt * hp <= fd::kFusedMaxHeads && (long long)gt * hp * splits <= fd::kFusedMaxRows &&
-                         (!p->work_list || p->persistent);
+    const bool fusable = page_size == 0 && splits <= fd::kFusedMaxSplits && slices <= fd::kFusedCounters &&
+                         gt * hp <= fd::kFusedMaxHeads && (long long)gt * hp * splits <= fd::kFusedMaxRows;
     if (splits <= 1) {
         p->merge = 0;
     } else if (forced_merge == FD_MERGE_FUSED) {
         if (!fusable)
-            return fail(FD_ERR_UNSUPPORTED, "this plan cannot merge in its last workgroups (%lld splits, %lld "
-                        "counters, work list %d)", splits, (long long)B * slices, p->work_list);
+            return fail(FD_ERR_UNSUPPORTED, "this plan cannot merge in its last workgroups (a contiguous cache "
+                        "of at most %d splits and %d (head, split) rows per workgroup: %lld splits, %lld rows%s)",
+                        fd::kFusedMaxSplits, fd::kFusedMaxRows, splits, (long long)gt * hp * splits,
+                        page_size > 0 ? ", paged" : "");
         p->merge = FD_MERGE_FUSED;
     } else if (forced_merge == FD_MERGE_KERNEL) {
         p->merge = FD_MERGE_KERNEL;
@@ -358,7 +367,7 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         a.ws_o = nullptr;
         a.ws_lse = nullptr;
     }
-    a.fused = plan.merge == FD_MERGE_FUSED ? 1 : 0;
+    const bool fused = plan.merge == FD_MERGE_FUSED;
     a.persistent = plan.persistent;
     a.slices = plan.head_slices;
     a.counters = plan.workspace_bytes > 0 ? reinterpret_cast<unsigned *>(ws) : nullptr;
@@ -376,9 +385,10 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
     const int mode = !paged ? fd::kContig : ((1 << a.page_shift) >= 16 ? fd::kPagedBlock : fd::kPagedRow);
     const bool persist = plan.persistent != 0;
     hipError_t e = plan.kernel == FD_KERNEL_MFMA
-                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, persist, shape, a, stream, ev0, ev1)
+                       ? fd::launch_split_mfma(dtype, plan.heads_per_group, mode, persist, fused, shape, a, stream,
+                                               ev0, ev1)
                        : fd::launch_split_valu(dtype, plan.heads_per_group, plan.kv_heads_per_group, mode, persist,
-                                               shape, a, stream, ev0, ev1);
+                                               fused, shape, a, stream, ev0, ev1);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "split kernel launch: %s", hipGetErrorString(e));
     if (plan.merge == FD_MERGE_KERNEL) {
         m.ws_o = a.ws_o;

@@ -403,6 +403,27 @@ __device__ __forceinline__ void store_out_pair(void *out, size_t bh, int lane, f
     reinterpret_cast<P2 *>(reinterpret_cast<T *>(out) + bh * kHeadDim)[lane] = Pair<T>::make(v.x, v.y);
 }
 
+// ---------------------------------------------------------------- split boundaries
+// A contiguous cache (one sequence; every split in one round of workgroups)
+// has max(1, floor(L / chunk)) splits: split s covers [s*chunk, (s+1)*chunk)
+// except the last, which runs to L and so also takes the remainder (chunk ..
+// 2*chunk - 1 tokens), so no short split straggles behind the others.
+// A paged batch has ceil(L / chunk) splits, the cut of "[CUDA 优化实战] 纯手搓
+// flash decoding sm120", section "1. flash decoding": all but the last hold
+// chunk tokens and the last the remainder (1 .. chunk tokens). Those short
+// splits are numbered last, largest first (paged item order below), so they
+// fill the end of a launch that would otherwise end on chunk-sized items.
+// Either way every token is covered once and no split is empty; L = 0 has none.
+template <bool PAGED>
+__device__ __forceinline__ int splits_of(int L, int chunk) {
+    if (L <= 0) return 0;
+    return PAGED ? (L + chunk - 1) / chunk : max(1, L / chunk);
+}
+
+__device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
+    return split == n - 1 ? L : (split + 1) * chunk;
+}
+
 // ---------------------------------------------------------------- split prologue
 // Length of sequence b and, for a paged cache, the split's slice of its block
 // table staged in LDS (entries clamped into [0, num_pages)). The table loads
@@ -419,8 +440,7 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
     } else {
         const int L_raw = a.seq_lens[b];
         const int first = t_begin >> a.page_shift;
-        // a split spans at most 2*chunk - 1 tokens (the last one takes the remainder)
-        const int last = min((t_begin + 2 * a.chunk - 2) >> a.page_shift, a.max_blocks - 1);
+        const int last = min((t_begin + a.chunk - 1) >> a.page_shift, a.max_blocks - 1);  // a split holds <= chunk tokens
         const int32_t *row = a.block_table + (size_t)b * a.max_blocks + first;
         for (int i = item_tid(); i <= last - first; i += kSplitThreads)
             s_pages[i] = min(max(row[i], 0), a.num_pages - 1);
@@ -433,9 +453,10 @@ __device__ __forceinline__ int split_prologue(const SplitArgs &a, int b, int t_b
 // ---------------------------------------------------------------- debug checks
 // With fd_options.debug_checks a paged split records the first out-of-range
 // value it meets (the kernels clamp either way, so no access leaves the cache):
-// the workgroup of a sequence's last split checks L_b against [0, max_len],
-// and every split checks the table entries of the blocks it reads. The
-// winner of the compare-and-swap on the kind word writes the rest.
+// the workgroup of a sequence's last split (or of the item that writes an empty
+// sequence's zeros) checks L_b against [0, max_len], and every split checks
+// the table entries of the blocks it reads. The winner of the compare-and-swap
+// on the kind word writes the rest.
 __device__ __forceinline__ void report_bad(int *err, int kind, int b, int index, int value) {
     if (atomicCAS(err, 0, kind) == 0) {
         err[1] = b;
@@ -445,10 +466,10 @@ __device__ __forceinline__ void report_bad(int *err, int kind, int b, int index,
 }
 
 // Every thread of the workgroup calls this (no barrier inside). The split reads
-// tokens [t_begin, t_end) (t_end <= t_begin when the split is empty); not_last
-// is 0 for the workgroup that owns the sequence's last split.
-__device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int t_begin, int t_end, int not_last) {
-    if (!not_last && item_tid() == 0) {
+// tokens [t_begin, t_end) (t_end <= t_begin when the split is empty); owns_len
+// is set for the one item of the sequence that checks its length.
+__device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int t_begin, int t_end, bool owns_len) {
+    if (owns_len && item_tid() == 0) {
         const int L_raw = a.seq_lens[b];
         if (L_raw < 0 || L_raw > a.max_len) report_bad(a.err, kBadSeqLen, b, 0, L_raw);
     }
@@ -461,44 +482,47 @@ __device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int
     }
 }
 
-// ---------------------------------------------------------------- split boundaries
-// A sequence of L tokens has max(1, floor(L / chunk)) splits (none if L = 0):
-// split s covers [s*chunk, (s+1)*chunk) except the last, which runs to L and so
-// also takes the remainder (chunk .. 2*chunk - 1 tokens, or all L < 2*chunk).
-__device__ __forceinline__ int splits_of(int L, int chunk) { return L <= 0 ? 0 : max(1, L / chunk); }
-
-__device__ __forceinline__ int split_end(int split, int n, int L, int chunk) {
-    return split == n - 1 ? L : (split + 1) * chunk;
-}
-
 // ---------------------------------------------------------------- paged item order
-// Sequence b of a paged batch has n_b = max(1, splits_of(L_b)) items (one item
-// writes the zeros of an empty sequence). Its last split also takes the
-// remainder, so it holds chunk to 2*chunk - 1 tokens while the others hold
-// exactly chunk: the last splits are the largest items. Workgroups start in
-// linear-id order, so the items are numbered largest first: items 0 .. B-1 are
-// the last splits of sequences 0 .. B-1, then come the other splits, sequence
-// by sequence. The batch then ends on equal-sized items instead of a random
-// mix of sizes (the longest-first rule of list scheduling); the splits
-// themselves, and so the results, do not change.
+// Sequence b of a paged batch holds f_b = floor(L_b / chunk) full splits of
+// chunk tokens and, when chunk does not divide L_b, a remainder split of
+// r_b = L_b - f_b * chunk tokens; an empty sequence holds one item that writes
+// its zeros. Workgroups start, and persistent workgroups claim, in item
+// order, and the items are numbered largest first (the longest-first rule of
+// list scheduling): the full splits, sequence by sequence, then the remainder
+// items by decreasing size (ties by sequence), the empty sequences last. The
+// splits themselves, and so the results, do not depend on the order.
+//
+// build_work_list fills s_full[b] = full splits of the sequences before b
+// (s_full[B] = F, their total) and s_rem[k] = the sequence of the k-th
+// remainder item, and returns the item count F + R. Every thread of the
+// workgroup must call this (it holds barriers). B <= kMaxListSeqs.
+struct WorkList {
+    int full[kMaxListSeqs + 1];
+    int rem[kMaxListSeqs];
+    int key[kMaxListSeqs];  // remainder size, 0 for an empty sequence, -1 for no remainder item
+    int wave[kSplitThreads / 64];
+    int rem_count;
+};
 
-// Work list (a batch far shorter than its longest sequence, with total_kv
-// known): grid y numbers only items that exist. s_start[b] = the non-last
-// splits of sequences before b, s_start[B] = their total, which is returned.
-// Every thread of the workgroup must call this (it holds barriers).
-// B <= kMaxListSeqs.
-__device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start, int *s_wave) {
+__device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    int cnt[4];
+    if (t == 0) w.rem_count = 0;
+    int cnt[4], key[4];
     int local = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
         const int bb = 4 * t + j;
-        int n = 0;
-        if (bb < a.B) n = max(1, splits_of(max(0, min(a.seq_lens[bb], a.max_len)), a.chunk)) - 1;
-        cnt[j] = n;
-        local += n;
+        cnt[j] = 0;
+        key[j] = -1;
+        if (bb < a.B) {
+            const int L = max(0, min(a.seq_lens[bb], a.max_len));
+            cnt[j] = L / a.chunk;
+            const int r = L - cnt[j] * a.chunk;
+            key[j] = (r > 0 || L == 0) ? r : -1;
+            w.key[bb] = key[j];
+        }
+        local += cnt[j];
     }
     int x = local;  // inclusive scan over the wave
 #pragma unroll
@@ -506,59 +530,75 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, int *s_start,
         const int y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
-    if (lane == 63) s_wave[wave] = x;
+    if (lane == 63) w.wave[wave] = x;
     __syncthreads();
     int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wave[w];
+    for (int v = 0; v < wave; ++v) base += w.wave[v];
     int excl = base + x - local;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int bb = 4 * t + j;
-        if (bb < a.B) s_start[bb] = excl;
+        if (bb < a.B) w.full[bb] = excl;
         excl += cnt[j];
     }
-    if (t == kSplitThreads - 1) s_start[a.B] = excl;  // the last thread's end is the total
+    if (t == kSplitThreads - 1) w.full[a.B] = excl;  // the last thread's end is the total
+    // Rank of each remainder item: items that are larger, or as large from an earlier sequence.
+    int rank[4] = {0, 0, 0, 0};
+    for (int bb = 0; bb < a.B; ++bb) {
+        const int kb = w.key[bb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rank[j] += (kb > key[j] || (kb == key[j] && bb < 4 * t + j)) ? 1 : 0;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (key[j] >= 0) {
+            w.rem[rank[j]] = 4 * t + j;
+            ++mine;
+        }
+    }
+    if (mine) atomicAdd(&w.rem_count, mine);
     __syncthreads();
-    return s_start[a.B];
+    return w.full[a.B] + w.rem_count;
 }
 
-// The sequence of the r-th non-last split: the largest b with s_start[b] <= r.
-// s_start does not decrease, and a sequence with no such split shares its
-// start with the next one, so the largest such b is the one holding r.
-__device__ __forceinline__ int find_sequence(const int *s_start, int B, int r) {
+// The sequence of the r-th full split: the largest b with full[b] <= r. full
+// does not decrease, and a sequence with no full split shares its start with
+// the next one, so the largest such b is the one holding r.
+__device__ __forceinline__ int find_sequence(const int *full, int B, int r) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_start[mid] <= r) lo = mid;
+        if (full[mid] <= r) lo = mid;
         else hi = mid - 1;
     }
     return lo;
 }
 
-// (sequence, split) of work-list item `item` < B + s_start[B].
-__device__ __forceinline__ void work_list_item(const int *s_start, int B, int item, int &b, int &split) {
-    if (item < B) {
-        b = item;
-        split = s_start[b + 1] - s_start[b];  // the last split: index n_b - 1
+// (sequence, split) of item `item` < F + R.
+__device__ __forceinline__ void work_list_item(const WorkList &w, int B, int item, int &b, int &split) {
+    const int F = w.full[B];
+    if (item < F) {
+        b = find_sequence(w.full, B, item);
+        split = item - w.full[b];
     } else {
-        const int r = item - B;
-        b = find_sequence(s_start, B, r);
-        split = r - s_start[b];
+        b = w.rem[item - F];
+        split = w.full[b + 1] - w.full[b];  // the remainder follows the full splits
     }
 }
 
 // When total_kv understated the batch, items past the grid have no workgroup.
 // Their results become NaN instead of silently missing: the output rows of
-// one-split sequences, and the LSE of the missing splits of the others (the
-// merge then yields NaN). Run by one workgroup.
+// sequences with at most one split, and the LSE of the missing splits of the
+// others (the merge then yields NaN). Run by one workgroup.
 template <typename T>
-__device__ void poison_unlisted(const SplitArgs &a, const int *s_start, int items) {
+__device__ void poison_unlisted(const SplitArgs &a, const WorkList &w, int items) {
     const float nan = __builtin_nanf("");
     for (int item = a.grid_items; item < items; ++item) {
         int b, split;
-        work_list_item(s_start, a.B, item, b, split);
-        const int n = s_start[b + 1] - s_start[b] + 1;
-        if (n == 1) {
+        work_list_item(w, a.B, item, b, split);
+        const int n = splits_of<true>(max(0, min(a.seq_lens[b], a.max_len)), a.chunk);
+        if (n <= 1) {
             T *o = reinterpret_cast<T *>(a.out) + (size_t)b * a.H * kHeadDim;
             for (int i = threadIdx.x; i < a.H * kHeadDim; i += kSplitThreads) o[i] = Elem<T>::store_cast(nan);
         } else {
@@ -568,43 +608,31 @@ __device__ void poison_unlisted(const SplitArgs &a, const int *s_start, int item
     }
 }
 
-// The item of a paged workgroup, in the order above. With a work list, grid y
-// is the item number. Otherwise the (splits x sequences) plane of the grid is
-// read as one index u = y + num_splits * z: u < B is the last split of
-// sequence u (its index needs L_u first), and u - B = (num_splits - 1) * b + s
-// is split s of sequence b, which the workgroup skips unless s < n_b - 1
-// (*not_last = 1; splits past a sequence's end are the grid's empty slots).
-// Returns false when the workgroup has nothing to do. Every thread of the
-// workgroup must call this (the work list holds barriers).
+// The item of a one-item-per-workgroup paged launch. With a work list, grid y
+// is the item number in the order above; otherwise grid y is the split and
+// grid z the sequence, and splits past a sequence's end are the grid's empty
+// slots (the item function finds them empty). Returns false when the
+// workgroup has nothing to do. Every thread of the workgroup must call this
+// (the work list holds barriers).
 template <typename T>
-__device__ __forceinline__ bool paged_item(const SplitArgs &a, int *s_start, int *s_wave, int &b, int &split,
-                                           int &not_last) {
-    not_last = 0;
+__device__ __forceinline__ bool paged_item(const SplitArgs &a, WorkList &w, int &b, int &split) {
     if (a.work_list) {
-        const int items = a.B + build_work_list(a, s_start, s_wave);
+        const int items = build_work_list(a, w);
         const int item = blockIdx.y;
         if (item == a.grid_items - 1 && blockIdx.x == 0 && items > a.grid_items)
-            poison_unlisted<T>(a, s_start, items);  // total_kv was short: fail loudly
+            poison_unlisted<T>(a, w, items);  // total_kv was short: fail loudly
         if (item >= items) return false;
-        work_list_item(s_start, a.B, item, b, split);
+        work_list_item(w, a.B, item, b, split);
         return true;
     }
-    const int u = blockIdx.y + a.num_splits * blockIdx.z;
-    if (u < a.B) {
-        b = u;
-        split = max(1, splits_of(max(0, min(a.seq_lens[b], a.max_len)), a.chunk)) - 1;
-    } else {
-        const int v = u - a.B;  // only reached when num_splits > 1
-        b = v / (a.num_splits - 1);
-        split = v - b * (a.num_splits - 1);
-        not_last = 1;
-    }
+    b = blockIdx.z;
+    split = blockIdx.y;
     return true;
 }
 
 // ---------------------------------------------------------------- paged item loop
-// The items of a paged workgroup, each handed to item(args, slice, b, split,
-// not_last). One item per workgroup (paged_item) unless the launch is persistent
+// The items of a paged workgroup, each handed to item(args, slice, b, split).
+// One item per workgroup (paged_item) unless the launch is persistent
 // (a separate kernel instantiation, PERSIST): then grid
 // x is one workgroup per resident slot, and each numbers the items once (the
 // work list) and claims them in item order, largest first, from a counter at the
@@ -632,17 +660,16 @@ __device__ __forceinline__ SplitArgs reload_args(const SplitArgs *s_args) {
 
 template <typename T, bool PERSIST, typename ItemFn>
 __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
-    __shared__ int s_start[kMaxListSeqs + 1];
-    __shared__ int s_wave[kSplitThreads / 64];
+    __shared__ WorkList s_list;
     if constexpr (!PERSIST) {
-        int b, split, not_last = 0;
-        if (paged_item<T>(a, s_start, s_wave, b, split, not_last)) item(a, blockIdx.x, b, split, not_last);
+        int b, split;
+        if (paged_item<T>(a, s_list, b, split)) item(a, blockIdx.x, b, split);
     } else {
         __shared__ int s_claim;
         __shared__ SplitArgs s_args;
         unsigned *const claims = a.counters + kQueueCounter;
         if (threadIdx.x == 0) s_args = a;
-        const int total = (a.B + build_work_list(a, s_start, s_wave)) * a.slices;
+        const int total = build_work_list(a, s_list) * a.slices;
         int claim = 0;  // thread 0: the claim in flight
         if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
         for (;;) {
@@ -654,8 +681,8 @@ __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
             if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
             const int u = q / a.slices;
             int b, split;
-            work_list_item(s_start, a.B, u, b, split);
-            item(reload_args(&s_args), q - u * a.slices, b, split, 0);
+            work_list_item(s_list, a.B, u, b, split);
+            item(reload_args(&s_args), q - u * a.slices, b, split);
         }
         if (threadIdx.x == 0) {
             const unsigned gone = atomicAdd(claims + 1, 1u) + 1u;
@@ -757,9 +784,7 @@ __device__ void fused_merge_tail(const SplitArgs &a, int slice, int b, int h0, i
     __syncthreads();
     if (!s_last) return;  // uniform over the workgroup
     // n_b rounded up to a compiled split count (at most kFusedMaxSplits)
-    if (n_b <= 4) fused_merge_rows<T, 4>(a, b, h0, nh, n_b);
-    else if (n_b <= 8) fused_merge_rows<T, 8>(a, b, h0, nh, n_b);
-    else if (n_b <= 16) fused_merge_rows<T, 16>(a, b, h0, nh, n_b);
+    if (n_b <= 8) fused_merge_rows<T, 8>(a, b, h0, nh, n_b);
     else fused_merge_rows<T, 32>(a, b, h0, nh, n_b);
 }
 
@@ -767,9 +792,10 @@ __device__ void fused_merge_tail(const SplitArgs &a, int slice, int b, int h0, i
 // split `split` of n_b. value(hh, d, lse) returns the split's normalised
 // output element and sets its natural-log lse. When n_b == 1 the split is the
 // whole sequence and o is written directly; otherwise the partial goes to the
-// workspace, for the merge kernel or (fused launch) for the last workgroup of
-// the sequence's head slice.
-template <typename T, typename ValueFn>
+// workspace, for the merge kernel or, in a fused launch (FUSED: a kernel
+// instantiation of its own, so the merge-kernel path carries none of this
+// code), for the last workgroup of the sequence's head slice.
+template <typename T, bool FUSED, typename ValueFn>
 __device__ void finish_split(const SplitArgs &a, int slice, int b, int h0, int nh, int split, int n_b,
                              ValueFn value) {
     const bool direct = n_b == 1;
@@ -781,7 +807,7 @@ __device__ void finish_split(const SplitArgs &a, int slice, int b, int h0, int n
         const size_t bh = (size_t)b * a.H + h0 + hh;
         if (direct) {
             reinterpret_cast<T *>(a.out)[bh * kHeadDim + d] = Elem<T>::store_cast(o);
-        } else if (a.fused) {
+        } else if (FUSED) {
             const size_t row = bh * a.num_splits + split;
             store_device(a.ws_o + row * kHeadDim + d, o);
             if (d == 0) store_device(a.ws_lse + row, lse);
@@ -791,7 +817,9 @@ __device__ void finish_split(const SplitArgs &a, int slice, int b, int h0, int n
             if (d == 0) a.ws_lse[row] = lse;
         }
     }
-    if (!direct && a.fused) fused_merge_tail<T>(a, slice, b, h0, nh, n_b);
+    if constexpr (FUSED) {
+        if (!direct) fused_merge_tail<T>(a, slice, b, h0, nh, n_b);
+    }
 }
 
 }  // namespace fd

@@ -44,10 +44,9 @@ struct SplitArgs {
     int work_list;          // 1: grid y numbers the splits that hold tokens (paged; see the split kernels)
     int grid_items;         // grid y when work_list is set
     int *err;               // paged with debug_checks: 4-int error record (kind, sequence, index, value); else NULL
-    unsigned *counters;     // workspace counter block: fused-merge counters per (sequence, head slice)
-                            // at its head, the persistent launch's claim and exit counters at its end;
-                            // all zero between calls
-    int fused;              // 1: the last workgroup of each (sequence, head slice) merges (no merge kernel)
+    unsigned *counters;     // workspace counter block: fused-merge counters per head slice at its
+                            // head, the persistent launch's claim and exit counters at its end; all
+                            // zero between calls
     int slices;             // head slices per sequence (grid x of a one-item-per-workgroup launch)
     int persistent;         // paged: 1 = one workgroup per resident slot, claiming items (see fd_device.h)
 };
@@ -95,12 +94,14 @@ struct LaunchShape {
 // Each returns hipSuccess or the launch error. `gt` = query heads per KV head in a
 // workgroup, `hp` = adjacent KV heads per workgroup (vector-ALU kernel, MHA),
 // `mode` = AddrMode of fd_device.h (contiguous, paged by 16-token block, paged by row);
-// `persist` (paged modes): one workgroup per resident slot claiming items.
+// `persist` (paged modes): one workgroup per resident slot claiming items;
+// `fused` (contiguous only): the last workgroup of each head slice merges.
 // `start`/`stop` (may be NULL) are timestamped by the dispatch itself at the
 // kernel's start and end (hipExtLaunchKernel), so they time the kernel alone.
-hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, bool persist, const LaunchShape &shape,
-                             const SplitArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
-hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, bool persist, const LaunchShape &shape,
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, bool persist, bool fused,
+                             const LaunchShape &shape, const SplitArgs &a, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop);
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, bool persist, bool fused, const LaunchShape &shape,
                              const SplitArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // Launch through hipExtLaunchKernel when events are given, else hipLaunchKernel.

@@ -6,8 +6,9 @@
 // is the merge of "[CUDA 优化实战] 纯手搓 flash decoding sm120", section "2. kernel
 // 实现细节" (weights exp(lse_s - global lse)) and equals the (m, l) form of
 // "FlashAttention 与推理算子", section "decode 阶段的并行：Flash-Decoding 与
-// split-K", since lse_s = m_s + ln l_s. Only the max(1, floor(L_b / chunk))
-// splits of sequence b are read (its last split also holds the remainder).
+// split-K", since lse_s = m_s + ln l_s. Only the splits sequence b has are read
+// (splits_of: ceil(L_b / chunk) for a paged batch, max(1, floor(S / chunk)) for a
+// contiguous cache).
 // Each lane owns two adjacent output elements, so a split's 512-byte partial
 // row is one coalesced 8-byte-per-lane load. Sequences with one split (or no
 // token) were written directly by the split kernel and are skipped here.
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     pin_args(a.ws_o, a.ws_lse, a.out, a.H);
     int L = a.max_len;
     if (PAGED) L = max(0, min(a.seq_lens[b], a.max_len));
-    const int n = min(splits_of(L, a.chunk), a.num_splits);
+    const int n = min(splits_of<PAGED>(L, a.chunk), a.num_splits);
     if (n <= 1) return;  // the split kernel wrote this row directly (zeros when L = 0)
     const size_t bh = (size_t)b * a.H + h;
     const float *ws_o_row = a.ws_o + bh * a.num_splits * kHeadDim;

@@ -147,9 +147,8 @@ struct KvFrag<T, fp8e4m3> {
     }
 };
 
-template <typename T, typename KV, int MODE>
-__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int slice, const int b, const int split,
-                                                const int not_last) {
+template <typename T, typename KV, int MODE, bool FUSED>
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int slice, const int b, const int split) {
     constexpr bool PAGED = MODE != kContig;
     using M = Mfma<T>;
     using F = KvFrag<T, KV>;
@@ -174,13 +173,14 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int sl
     const int t_begin = split * a.chunk;
     int page_first = 0;
     const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
-    const int n_b = splits_of(L, a.chunk);
+    const int n_b = splits_of<PAGED>(L, a.chunk);
     if constexpr (PAGED) {
         if (a.err != nullptr)
-            check_paged_split(a, b, t_begin, split < n_b ? split_end(split, n_b, L, a.chunk) : t_begin, not_last);
+            check_paged_split(a, b, t_begin, split < n_b ? split_end(split, n_b, L, a.chunk) : t_begin,
+                              split == max(n_b - 1, 0));
     }
-    if (split >= n_b - not_last) {  // uniform over the workgroup
-        if (split == 0 && !not_last) {  // empty sequence: o = 0
+    if (split >= n_b) {  // uniform over the workgroup
+        if (split == 0) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = tid; i < nh * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
@@ -382,7 +382,7 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int sl
         }
     }
     __syncthreads();
-    finish_split<T>(a, slice, b, h0, nh, split, n_b, [&](int hh, int d, float &lse) {
+    finish_split<T, FUSED>(a, slice, b, h0, nh, split, n_b, [&](int hh, int d, float &lse) {
         float Mx = s_m[0][hh];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][hh]);
@@ -403,31 +403,34 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const int sl
 // (sequence, split) items largest first, the last split of every sequence
 // before the others, one per workgroup or, in a persistent launch, claimed by
 // one workgroup per resident slot (paged_items).
-template <typename T, typename KV, int MODE, bool PERSIST>
+template <typename T, typename KV, int MODE, bool PERSIST, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma_kernel(SplitArgs a) {
     pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
     if constexpr (MODE == kContig) {
-        split_mfma_item<T, KV, MODE>(a, blockIdx.x, 0, blockIdx.y, 0);
+        split_mfma_item<T, KV, MODE, FUSED>(a, blockIdx.x, 0, blockIdx.y);
     } else {
-        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split, int not_last) {
-            split_mfma_item<T, KV, MODE>(ai, x, b, split, not_last);
+        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split) {
+            split_mfma_item<T, KV, MODE, false>(ai, x, b, split);
         });
     }
 }
 
-template <typename T, typename KV, int MODE, bool PERSIST>
+template <typename T, typename KV, int MODE, bool PERSIST, bool FUSED = false>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, KV, MODE, PERSIST>), s, args, st, e0,
-                        e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_mfma_kernel<T, KV, MODE, PERSIST, FUSED>), s, args, st,
+                        e0, e1);
 }
 
 template <typename T, typename KV>
-hipError_t launch_mode(int mode, bool persist, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
-                       hipEvent_t e1) {
+hipError_t launch_mode(int mode, bool persist, bool fused, const LaunchShape &s, const SplitArgs &a, hipStream_t st,
+                       hipEvent_t e0, hipEvent_t e1) {
+    if (fused && mode != kContig) return hipErrorInvalidValue;
     switch (mode) {
-        case kContig: return launch_one<T, KV, kContig, false>(s, a, st, e0, e1);
+        case kContig:
+            return fused ? launch_one<T, KV, kContig, false, true>(s, a, st, e0, e1)
+                         : launch_one<T, KV, kContig, false, false>(s, a, st, e0, e1);
         case kPagedBlock:
             return persist ? launch_one<T, KV, kPagedBlock, true>(s, a, st, e0, e1)
                            : launch_one<T, KV, kPagedBlock, false>(s, a, st, e0, e1);
@@ -440,14 +443,14 @@ hipError_t launch_mode(int mode, bool persist, const LaunchShape &s, const Split
 
 }  // namespace
 
-hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, bool persist, const LaunchShape &s, const SplitArgs &a,
-                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_split_mfma(fd_dtype dtype, int gt, int mode, bool persist, bool fused, const LaunchShape &s,
+                             const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if (gt < 1 || gt > kMaxHeads) return hipErrorInvalidValue;
     switch (dtype) {
-        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, s, a, st, e0, e1);
-        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, s, a, st, e0, e1);
-        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, fused, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, fused, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, fused, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, fused, s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

@@ -44,9 +44,8 @@ constexpr int kWaves = kThreads / 64;
 // token stride stream markedly slower than the same bytes in 512-B runs
 // (measured with a plain read kernel on the 32-head layout: 12.7 against 10.8 us
 // for 64 MB).
-template <typename T, typename KV, int GT, int HP, int MODE>
-__device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int slice, const int b, const int split,
-                                                const int not_last) {
+template <typename T, typename KV, int GT, int HP, int MODE, bool FUSED>
+__device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int slice, const int b, const int split) {
     static_assert(HP == 1 || GT == 1, "packed KV heads are for MHA");
     constexpr bool PAGED = MODE != kContig;
     using E = Elem<T>;
@@ -83,13 +82,14 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int sl
     const int t_begin = split * a.chunk;
     int page_first = 0;
     const int L = split_prologue<PAGED>(a, b, t_begin, s_pages, &page_first);
-    const int n_b = splits_of(L, a.chunk);
+    const int n_b = splits_of<PAGED>(L, a.chunk);
     if constexpr (PAGED) {
         if (a.err != nullptr)
-            check_paged_split(a, b, t_begin, split < n_b ? split_end(split, n_b, L, a.chunk) : t_begin, not_last);
+            check_paged_split(a, b, t_begin, split < n_b ? split_end(split, n_b, L, a.chunk) : t_begin,
+                              split == max(n_b - 1, 0));
     }
-    if (split >= n_b - not_last) {  // uniform over the workgroup
-        if (split == 0 && !not_last) {  // empty sequence: o = 0
+    if (split >= n_b) {  // uniform over the workgroup
+        if (split == 0) {  // empty sequence: o = 0
             T *o = reinterpret_cast<T *>(a.out) + ((size_t)b * a.H + h0) * kHeadDim;
             for (int i = tid; i < NH * kHeadDim; i += kThreads) o[i] = E::store_cast(0.f);
         }
@@ -285,7 +285,7 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int sl
     __syncthreads();
 
     // Merge the waves, then store the split (or the merged output).
-    finish_split<T>(a, slice, b, h0, NH, split, n_b, [&](int gi, int d, float &lse) {
+    finish_split<T, FUSED>(a, slice, b, h0, NH, split, n_b, [&](int gi, int d, float &lse) {
         float M = s_m[0][gi];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gi]);
@@ -306,49 +306,52 @@ __device__ __forceinline__ void split_valu_item(const SplitArgs &a, const int sl
 // (sequence, split) items largest first, the last split of every sequence
 // before the others, one per workgroup or, in a persistent launch, claimed by
 // one workgroup per resident slot (paged_items).
-template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST>
+template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST, bool FUSED>
 __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
     pin_args(a.q, a.k, a.v, a.ws_o, a.ws_lse, a.scale_log2);
     if constexpr (MODE == kContig) {
-        split_valu_item<T, KV, GT, HP, MODE>(a, blockIdx.x, 0, blockIdx.y, 0);
+        split_valu_item<T, KV, GT, HP, MODE, FUSED>(a, blockIdx.x, 0, blockIdx.y);
     } else {
-        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split, int not_last) {
-            split_valu_item<T, KV, GT, HP, MODE>(ai, x, b, split, not_last);
+        paged_items<T, PERSIST>(a, [&](const SplitArgs &ai, int x, int b, int split) {
+            split_valu_item<T, KV, GT, HP, MODE, false>(ai, x, b, split);
         });
     }
 }
 
-template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST>
+template <typename T, typename KV, int GT, int HP, int MODE, bool PERSIST, bool FUSED = false>
 hipError_t launch_one(const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     SplitArgs arg = a;
     void *args[] = {&arg};
-    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, KV, GT, HP, MODE, PERSIST>), s, args, st,
-                        e0, e1);
+    return launch_timed(reinterpret_cast<const void *>(&split_valu_kernel<T, KV, GT, HP, MODE, PERSIST, FUSED>), s,
+                        args, st, e0, e1);
 }
 
-template <typename T, typename KV, int MODE, bool PERSIST>
+template <typename T, typename KV, int MODE, bool PERSIST, bool FUSED = false>
 hipError_t launch_gt(int gt, int hp, const LaunchShape &s, const SplitArgs &a, hipStream_t st, hipEvent_t e0,
                      hipEvent_t e1) {
-    if (hp == 2 && gt == 1) return launch_one<T, KV, 1, 2, MODE, PERSIST>(s, a, st, e0, e1);
-    if (hp == 4 && gt == 1) return launch_one<T, KV, 1, 4, MODE, PERSIST>(s, a, st, e0, e1);
+    if (hp == 2 && gt == 1) return launch_one<T, KV, 1, 2, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
+    if (hp == 4 && gt == 1) return launch_one<T, KV, 1, 4, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
     if (hp != 1) return hipErrorInvalidValue;
     switch (gt) {
-        case 1: return launch_one<T, KV, 1, 1, MODE, PERSIST>(s, a, st, e0, e1);
-        case 2: return launch_one<T, KV, 2, 1, MODE, PERSIST>(s, a, st, e0, e1);
-        case 4: return launch_one<T, KV, 4, 1, MODE, PERSIST>(s, a, st, e0, e1);
+        case 1: return launch_one<T, KV, 1, 1, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
+        case 2: return launch_one<T, KV, 2, 1, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
+        case 4: return launch_one<T, KV, 4, 1, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
         case 8:
             // fp32 rows stop at 4 heads per workgroup (the planner never asks for 8)
             if constexpr (std::is_same<T, float>::value) return hipErrorInvalidValue;
-            else return launch_one<T, KV, 8, 1, MODE, PERSIST>(s, a, st, e0, e1);
+            else return launch_one<T, KV, 8, 1, MODE, PERSIST, FUSED>(s, a, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, typename KV>
-hipError_t launch_mode(int mode, bool persist, int gt, int hp, const LaunchShape &s, const SplitArgs &a,
+hipError_t launch_mode(int mode, bool persist, bool fused, int gt, int hp, const LaunchShape &s, const SplitArgs &a,
                        hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    if (fused && mode != kContig) return hipErrorInvalidValue;
     switch (mode) {
-        case kContig: return launch_gt<T, KV, kContig, false>(gt, hp, s, a, st, e0, e1);
+        case kContig:
+            return fused ? launch_gt<T, KV, kContig, false, true>(gt, hp, s, a, st, e0, e1)
+                         : launch_gt<T, KV, kContig, false, false>(gt, hp, s, a, st, e0, e1);
         case kPagedBlock:
             return persist ? launch_gt<T, KV, kPagedBlock, true>(gt, hp, s, a, st, e0, e1)
                            : launch_gt<T, KV, kPagedBlock, false>(gt, hp, s, a, st, e0, e1);
@@ -361,14 +364,14 @@ hipError_t launch_mode(int mode, bool persist, int gt, int hp, const LaunchShape
 
 }  // namespace
 
-hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, bool persist, const LaunchShape &s,
+hipError_t launch_split_valu(fd_dtype dtype, int gt, int hp, int mode, bool persist, bool fused, const LaunchShape &s,
                              const SplitArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (dtype) {
-        case FD_DTYPE_F32: return launch_mode<float, float>(mode, persist, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, gt, hp, s, a, st, e0, e1);
-        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F32: return launch_mode<float, float>(mode, persist, fused, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F16: return launch_mode<_Float16, _Float16>(mode, persist, fused, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_BF16: return launch_mode<__bf16, __bf16>(mode, persist, fused, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_F16_KV_E4M3: return launch_mode<_Float16, fp8e4m3>(mode, persist, fused, gt, hp, s, a, st, e0, e1);
+        case FD_DTYPE_BF16_KV_E4M3: return launch_mode<__bf16, fp8e4m3>(mode, persist, fused, gt, hp, s, a, st, e0, e1);
     }
     return hipErrorInvalidValue;
 }

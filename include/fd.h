@@ -111,7 +111,8 @@ typedef struct fd_options {
     void *split_end_event;   /* hipEvent_t stamped when the split kernel finishes, or NULL
                                 (both set by the dispatch itself: hipExtLaunchKernel) */
     int force_merge;         /* FD_MERGE_*: how the partials of a multi-split plan are merged;
-                                FD_MERGE_FUSED where the plan cannot fuse is FD_ERR_UNSUPPORTED */
+                                FD_MERGE_FUSED is for contiguous caches (at most 32 splits and 64
+                                (head, split) rows per workgroup), elsewhere FD_ERR_UNSUPPORTED */
     int force_launch;        /* FD_LAUNCH_*: paged calls only (contiguous ones launch a grid);
                                 FD_LAUNCH_PERSISTENT needs B <= 1024, else FD_ERR_UNSUPPORTED */
 } fd_options;
@@ -121,7 +122,8 @@ typedef struct fd_plan {
     int kernel;          /* FD_KERNEL_VALU or FD_KERNEL_MFMA */
     int heads_per_group; /* query heads of one KV head that one workgroup computes (they share its rows) */
     int chunk;           /* split stride: every split but a sequence's last holds this many tokens */
-    int num_splits;      /* splits of the longest sequence, max(1, floor(max_len / chunk)) = grid y */
+    int num_splits;      /* splits of the longest sequence = grid y: ceil(max_len / chunk) for a paged
+                            batch, max(1, floor(S / chunk)) for a contiguous cache (at least 1) */
     int grid_x, grid_y, grid_z; /* split kernel grid: (head_slices, splits, sequences); see work_list
                                    and persistent */
     int threads;         /* split kernel workgroup size */
@@ -132,10 +134,11 @@ typedef struct fd_plan {
                                H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0 and no debug record) */
     size_t ws_lse_offset;   /* byte offset of ws_lse inside the workspace */
-    int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens (the last
-                               split of every sequence first, then the others sequence by sequence),
-                               grid_z = 1, one split per workgroup; chosen when the (splits x
-                               sequences) grid would be mostly empty splits and total_kv is known */
+    int work_list;          /* 1 (paged only): grid_y numbers the splits that hold tokens (the full
+                               splits sequence by sequence, then the remainder splits largest first,
+                               empty sequences last), grid_z = 1, one split per workgroup; chosen
+                               when the (splits x sequences) grid would be mostly empty splits and
+                               total_kv is known */
     int persistent;         /* 1 (paged only): grid_x = one workgroup per resident slot (two per compute
                                unit), grid_y = grid_z = 1; every workgroup numbers the items as the work
                                list does and claims them, largest first, from a counter in the
@@ -172,18 +175,20 @@ typedef struct fd_plan {
  *                                scores, at byte offset ws_lse_offset.
  * ws_o and ws_lse need no initialisation; the debug record, when asked for,
  * follows at ws_err_offset and is cleared by the call itself.
- * Sequence b has n_b = max(1, floor(L_b / chunk)) splits (none when L_b = 0).
- * Split s < n_b - 1 covers tokens [s*chunk, (s+1)*chunk); the last split covers
- * [(n_b - 1)*chunk, L_b), i.e. chunk to 2*chunk - 1 tokens (fewer only when it is
- * the only split), so no split is a short remainder. Only the splits of
- * sequences with n_b > 1 are written; a sequence with one split is written to
- * o directly (and in a fused launch the last split's workgroup merges). The
- * pages cut a sequence into ceil(L_b / chunk) splits with a
- * short last one; folding the remainder into the last full split gives the
- * same result up to rounding and spares a workgroup that would read few
- * tokens for a full workgroup's fixed cost. The split
- * kernel stores partials as "[CUDA 优化实战] 纯手搓 flash decoding sm120",
- * section "2. kernel 实现细节" describes: normalised output plus log-sum-exp.
+ * Split s < n_b - 1 of a sequence covers tokens [s*chunk, (s+1)*chunk) and the
+ * last split runs to the sequence's end. A paged sequence of L_b tokens has
+ * n_b = ceil(L_b / chunk) splits, the cut of "[CUDA 优化实战] 纯手搓 flash decoding
+ * sm120", section "1. flash decoding": the last one holds the remainder (1 ..
+ * chunk tokens); a batch's short remainder splits are scheduled last, largest
+ * first, and fill the end of the launch. A contiguous cache of S tokens (one
+ * sequence, every split in one round of workgroups) has max(1, floor(S /
+ * chunk)) splits, the last one also taking the remainder (chunk .. 2*chunk - 1
+ * tokens), so no short split straggles. Either way L = 0 has no split. Only
+ * the splits of sequences with n_b > 1 are written; a sequence with one split
+ * is written to o directly (and in a fused launch the last split's workgroup
+ * merges). The split kernel stores partials as "[CUDA 优化实战] 纯手搓 flash
+ * decoding sm120", section "2. kernel 实现细节" describes: normalised output plus
+ * log-sum-exp.
  */
 
 /* Compute units of the current HIP device (cached per device); -1 on error. */

@@ -44,10 +44,12 @@ def test_status_strings():
     assert lib.fd_status_string(99).decode() == "FD_ERR_UNKNOWN"
 
 
-def _check_plan(p, max_len, B, H, Hkv, G_heads=None):
+def _check_plan(p, max_len, B, H, Hkv, paged=False):
     assert p["chunk"] % 16 == 0 and p["chunk"] >= 16  # whole 16-token addressing blocks
-    # floor: the last split of a sequence also takes the remainder
-    assert p["num_splits"] == max(1, max_len // p["chunk"])
+    if paged:  # ceil: the last split of a sequence holds the remainder
+        assert p["num_splits"] == max(1, -(-max_len // p["chunk"]))
+    else:  # floor: the last split of the cache also takes the remainder
+        assert p["num_splits"] == max(1, max_len // p["chunk"])
     gt, hp = p["heads_per_group"], p["kv_heads_per_group"]
     assert (H // Hkv) % gt == 0 and Hkv % hp == 0 and (hp == 1 or H == Hkv)
     slices = (Hkv // hp) * (H // Hkv) // gt
@@ -78,7 +80,7 @@ def test_plan_of_each_workload(name):
     else:
         L = w.seq_lens()
         p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
-        _check_plan(p, int(L.max()), w.B, w.H, w.Hkv)
+        _check_plan(p, int(L.max()), w.B, w.H, w.Hkv, paged=True)
         assert p["heads_per_group"] == w.H // w.Hkv  # KV read once per group of q heads
 
 
@@ -110,7 +112,7 @@ def test_plan_work_list_choice():
     p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256, grid)
     assert p["work_list"] == 1 and p["grid_z"] == 1 and p["persistent"] == 0
     assert p["grid_y"] == w.B + int(L.sum()) // p["chunk"]
-    assert p["grid_y"] >= sum(max(1, int(x) // p["chunk"]) for x in L)  # every split has a workgroup
+    assert p["grid_y"] >= sum(max(1, -(-int(x) // p["chunk"])) for x in L)  # every split has a workgroup
     # by default the same items are claimed by one workgroup per resident slot
     d = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
     assert d["persistent"] == 1 and d["grid_x"] == 512 and d["chunk"] == p["chunk"]
@@ -142,7 +144,7 @@ def test_plan_paged_strides_of_the_batches():
 def test_plan_paged_chunk_fits_block_table_stage():
     for ps in (1, 2, 16, 64, 256, 1024):
         p = fd.paged_plan(2, 8, 8, "bf16", ps, 1 << 20, 2 << 20, 256)
-        pages = (2 * p["chunk"] - 2) // ps + 2  # a split spans up to 2*chunk - 1 tokens
+        pages = (p["chunk"] - 1) // ps + 2  # a paged split spans at most chunk tokens
         assert pages <= 1024
     with pytest.raises(fd.FdError) as e:
         fd.paged_plan(2, 8, 8, "bf16", 1, 100000, 0, 256, fd.options(force_chunk=2048))
@@ -323,8 +325,9 @@ def test_debug_record_in_the_paged_plan():
 
 def test_merge_choice():
     """Multi-split plans merge with the merge kernel unless the fused merge (the last
-    workgroups merge, one launch) is asked for; it is available up to 32 splits per
-    sequence on the full grid, and asking for it elsewhere is refused."""
+    workgroups merge, one launch) is asked for; it is available for a contiguous cache
+    up to 32 splits and 64 (head, split) rows per workgroup, and asking for it
+    elsewhere (more splits, a paged batch in either launch form) is refused."""
     for name in ("decode_f32_h8_s512", "decode_bf16_h32_s4096", "decode_bf16_h32_s131072_peaked"):
         w = WORKLOADS[name]
         p = fd.decode_plan(w.H, w.Hkv, w.S, w.dtype, 256)
@@ -343,6 +346,15 @@ def test_merge_choice():
         L = w.seq_lens()
         p = fd.paged_plan(w.B, w.H, w.Hkv, w.dtype, w.page_size, int(L.max()), int(L.sum()), 256)
         assert p["merge"] == 1
+    for launch in ("grid", "persistent"):
+        for total in (0, 20000):
+            with pytest.raises(fd.FdError) as e:
+                fd.paged_plan(8, 32, 8, "bf16", 16, 4000, total, 256,
+                              fd.options(force_chunk=256, merge="fused", launch=launch))
+            assert e.value.name == "FD_ERR_UNSUPPORTED" and "paged" in str(e.value)
+    with pytest.raises(fd.FdError) as e:  # 8 heads x 15 splits: more rows than one workgroup merges
+        fd.decode_plan(32, 4, 3000, "bf16", 256, fd.options(force_chunk=192, merge="fused"))
+    assert e.value.name == "FD_ERR_UNSUPPORTED"
     assert fd.decode_plan(8, 8, 100, "f32", 256, fd.options(force_num_splits=1))["merge"] == 0
     with pytest.raises(fd.FdError):
         fd.decode_plan(8, 8, 512, "f32", 256, fd.options(merge=3))

@@ -230,10 +230,26 @@ def test_partials_of_long_peaked(device, long_peaked):
 
 
 def kernel_split_bounds(L: int, chunk: int) -> list:
-    """Token ranges of the library's splits (include/fd.h, workspace layout):
-    max(1, floor(L / chunk)) splits, the last one running to L."""
+    """Token ranges of the library's splits of a contiguous cache (include/fd.h,
+    workspace layout): max(1, floor(L / chunk)) splits, the last one running to L."""
     n = max(1, L // chunk) if L > 0 else 0
     return [(s * chunk, L if s == n - 1 else (s + 1) * chunk) for s in range(n)]
+
+
+def paged_split_bounds(L: int, chunk: int) -> list:
+    """Token ranges of the library's splits of a paged sequence: ceil(L / chunk)
+    splits, the last one holding the remainder."""
+    return [(s, min(s + chunk, L)) for s in range(0, L, chunk)]
+
+
+def paged_item_order(lens, chunk: int) -> list:
+    """(sequence, split) of every item of a paged batch in the library's item order:
+    the full splits sequence by sequence, then the remainder splits by decreasing
+    size (ties by sequence), the empty sequences last."""
+    items = [(b, s) for b, L in enumerate(lens) for s in range(L // chunk)]
+    rem = [(L % chunk if L else 0, b) for b, L in enumerate(lens) if L % chunk or L == 0]
+    rem.sort(key=lambda kb: (-kb[0], kb[1]))
+    return items + [(b, lens[b] // chunk) for _, b in rem]
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
@@ -543,16 +559,15 @@ def test_work_list_short_total_is_nan(device):
     numbers the items on the device and gets every sequence right."""
     lens, d = _ragged_batch(48, 430)
     opt = fd.options(force_chunk=256, launch="grid")
-    short = sum(lens) // 3
+    # The work-list grid holds B + total_kv // chunk items, taken in the library's
+    # item order; a total_kv that leaves out the five smallest remainder splits
+    # (the empty sequence's item among them) cuts exactly those five sequences.
+    order = paged_item_order(lens, 256)
+    short = (len(order) - 5 - 48) * 256
     plan = fd.paged_plan(48, 32, 8, "bf16", 16, max(lens), short, 0, opt)
-    assert plan["work_list"] == 1
-    # Items: the last split of each of the 48 sequences first, then the other
-    # splits sequence by sequence; the grid holds the first grid_y of them.
-    others = [max(1, L // 256) - 1 for L in lens]
-    start = 48 + np.concatenate([[0], np.cumsum(others)])
-    assert plan["grid_y"] >= 48
-    missing = [b for b in range(48) if others[b] > 0 and start[b + 1] > plan["grid_y"]]
-    assert missing and len(missing) < 48
+    assert plan["work_list"] == 1 and plan["grid_y"] == len(order) - 5
+    missing = sorted({b for b, _ in order[plan["grid_y"]:]})
+    assert len(missing) == 5 and 3 in missing
     g = to_dev(d, device)
     outs = []
     for tk in (short, 0):
@@ -702,7 +717,7 @@ def test_paged_partials(kernel, work_list, launch, device):
     ws_o, ws_lse = fd.workspace_views(ws, plan, B, H)
     checked = 0
     for b, L in enumerate(lens):
-        bounds = kernel_split_bounds(L, chunk)
+        bounds = paged_split_bounds(L, chunk)
         if len(bounds) <= 1:
             continue  # one split: written to o directly
         kb = oracle.gather_pages(d["k_cache"], d["block_table"][b], L, 16)
@@ -868,40 +883,3 @@ def test_fused_merge_repeated_calls(device):
     for j, d in enumerate(ds):
         ref, _ = oracle.decode_attention(d["q"], d["k"], d["v"], d["scale"])
         assert_close(first[j], ref, "bf16", f"input {j}")
-
-
-def test_fused_paged_grid(device):
-    """A paged batch on the full (split, sequence) grid with the fused merge forced
-    (counters per sequence and head slice), against the oracle; a work-list plan
-    cannot fuse and says so."""
-    lens = [5, 300, 1500, 4000, 2049, 0, 64, 3333]
-    d = inputs.paged_inputs(len(lens), 32, 8, 128, "bf16", 16, lens, 997)
-    ref, _ = oracle.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
-                                           16, d["scale"])
-    g = to_dev(d, device)
-    for kernel in ("mfma", "valu"):
-        opt = fd.options(force_chunk=256, kernel=kernel, merge="fused")
-        plan = fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), 0, 0, opt)
-        assert plan["merge"] == 2 and plan["work_list"] == 0
-        ws = poisoned_workspace(plan["workspace_bytes"], device)
-        announce(f"fused paged grid {kernel}")
-        o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
-                               scale=d["scale"], max_seq_len=max(lens), total_kv=0, opt=opt, ws=ws)
-        torch.cuda.synchronize()
-        assert_close(o, ref, "bf16", f"fused paged {kernel}")
-        assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)
-    with pytest.raises(fd.FdError) as e:
-        fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), sum(lens), 0,
-                      fd.options(force_chunk=256, merge="fused", launch="grid"))
-    assert e.value.name == "FD_ERR_UNSUPPORTED"
-    # a persistent launch processes every item, so its work list can fuse
-    opt = fd.options(force_chunk=256, merge="fused", launch="persistent")
-    plan = fd.paged_plan(len(lens), 32, 8, "bf16", 16, max(lens), sum(lens), 0, opt)
-    assert plan["merge"] == 2 and plan["work_list"] == 1 and plan["persistent"] == 1
-    ws = poisoned_workspace(plan["workspace_bytes"], device)
-    announce("fused paged persistent work list")
-    o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
-                           scale=d["scale"], max_seq_len=max(lens), total_kv=sum(lens), opt=opt, ws=ws)
-    torch.cuda.synchronize()
-    assert_close(o, ref, "bf16", "fused paged persistent")
-    assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0)

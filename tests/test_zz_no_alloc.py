@@ -79,16 +79,19 @@ def test_noalloc_two_calls_match_paged_decode(device):
         check(o, d)
 
 
-def test_noalloc_fused_merge_uses_the_scratch_counters(device):
-    """The fused merge keeps its counters at the head of the static scratch: two calls
-    in a row (the second smaller) give the bits of the same plan on a workspace."""
-    for lens, seed in (([300, 4000, 2049, 64, 3333], 64), ([700, 1500], 65)):
+def test_noalloc_persistent_launch_uses_the_scratch_counters(device):
+    """The persistent launch claims its items through two counters in the block at the
+    head of the static scratch, which its last workgroup returns to zero: two calls in
+    a row (the second smaller) give the bits of the same plan on a workspace."""
+    for lens, seed in (([300, 4000, 2049, 64, 3333, 0, 17], 64), ([700, 1500], 65)):
         d = inputs.paged_inputs(len(lens), 32, 8, 128, "bf16", 16, lens, seed)
         g = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
-        opt = fd.options(force_chunk=256, merge="fused")
-        announce(f"fused, {len(lens)} sequences")
-        o = noalloc(g, d, opt=opt, total_kv=0)
-        ref = with_workspace(g, d, opt=opt, total_kv=0)
+        opt = fd.options(force_chunk=256, launch="persistent")
+        plan = fd.paged_plan(d["B"], 32, 8, "bf16", 16, d["max_seq_len"], d["total_kv"], 0, opt)
+        assert plan["persistent"] == 1
+        announce(f"persistent, {len(lens)} sequences, work list {plan['work_list']}")
+        o = noalloc(g, d, opt=opt)
+        ref = with_workspace(g, d, opt=opt)
         torch.cuda.synchronize()
         assert torch.equal(o, ref)
         check(o, d)
