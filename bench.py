@@ -472,11 +472,11 @@ def main() -> int:
         copy_probe(args.copy_probe, args.steps)
         return 0
 
-    from decode_attention_13_amd.inputs import PREFILL_WORKLOADS, WORKLOADS, sweep_workload
+    from decode_attention_13_amd.inputs import CHOICE_WORKLOADS, PREFILL_WORKLOADS, WORKLOADS, sweep_workload
     if args.workload in PREFILL_WORKLOADS:
         print(json.dumps(bench_prefill(args)), flush=True)
         return 0
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[args.workload] if args.workload in WORKLOADS else CHOICE_WORKLOADS[args.workload]
     case = Case(w, args.chunk, args.kernel, kv=args.kv, merge=args.merge, launch=args.launch)
     split_kernel = SPLIT_KERNELS[case.plan["kernel"]]
     wl_name = w.name + ("_kv_e4m3" if case.fp8 else "")

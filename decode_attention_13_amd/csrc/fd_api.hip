@@ -70,10 +70,16 @@ int target_wgs_per_cu(fd_dtype dtype, bool mha, long long kv_bytes) {
 // workgroup first loads every sequence length and numbers the items (a prefix
 // sum and two barriers) before it can load its table slice: one more dependent
 // round trip, and a larger fixed cost. Measured on the GQA4 batch (grid) and
-// the GQA8 batch (work list), bf16/f16 and E4M3 caches, with the largest items
-// started first: best strides 1024 and 4096 (2048 for the GQA8 batch cost 2.2%
-// on the 16-bit cache and 2.5% on the E4M3 cache).
+// the GQA8 batch (work list), bf16/f16 caches, with the largest items started
+// first: best strides 1024 and 4096 (2048 for the GQA8 batch cost 2.2%).
 constexpr double kWgFixedBytes = 32768.0;
+// An E4M3 cache halves the bytes of a token but not the per-page and per-split
+// work around them (table entries, addresses, the scale, the partial store), so
+// its fixed cost is worth twice as many bytes: on the GQA4 batch the split kernel
+// ran 117.6 us at 2048 tokens against 125.5 us at 1024, and on the GQA8 batch
+// 8192 tokens matched 4096 in the split kernel and saved 2.4% of the step (fewer
+// partials to merge).
+constexpr double kWgFixedFp8Scale = 2.0;
 constexpr double kWgFixedBytesList = 3.0 * kWgFixedBytes;
 constexpr int kPagedSlotsPerCu = 2;  // resident split workgroups per CU (two waves per SIMD)
 constexpr int kMinChunk = 16;  // one 16-token block: a short cache still spreads over many workgroups
@@ -188,7 +194,9 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
         const double row_bytes = 2.0 * FD_HEAD_DIM * cache_elem_bytes(dtype) * hp;  // K + V of one token, per workgroup
         const double per_slot =
             (double)std::max(total, 1LL) * (Hkv / hp) * row_bytes / ((double)num_cus * kPagedSlotsPerCu);
+        const double fixed_scale = fd::is_fp8_cache(dtype) ? kWgFixedFp8Scale : 1.0;
         auto balanced = [&](double fixed_bytes) {
+            fixed_bytes *= fixed_scale;
             const double tokens = std::sqrt(2.0 * per_slot * fixed_bytes) / row_bytes;
             const long long c = 1LL << std::max(0L, std::lround(std::log2(std::max(tokens, 1.0))));  // nearest power of two
             return std::min<long long>(std::max<long long>(c, kMinChunk), kMaxChunk);
@@ -272,15 +280,15 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
             p->grid_z = 1;
         }
     }
-    // Merge of the partials. A fused launch needs a counter per (sequence, head
-    // slice) in the workspace's head block and merges at most kFusedMaxSplits
-    // splits in one workgroup; a work-list launch keeps the merge kernel (the
-    // splits that total_kv leaves without a workgroup must still come out NaN).
-    // The merge kernel is the default: on the 4k-token 32-head decode the fused
-    // step measured 17.2 us against 15.1 us. Its tail (partial stores written
-    // through to memory, a wait for them, a counter round trip, the reads of the
-    // last workgroup) costs about 2.4 us on every workgroup's critical path,
-    // while the merge kernel after the split kernel adds only 0.4 us to a step.
+    // Merge of the partials. A fused launch (contiguous caches only) needs a
+    // counter per head slice in the workspace's head block and merges at most
+    // kFusedMaxSplits splits in one workgroup. The merge kernel is the default:
+    // on the 4k-token 32-head decode the fused step measured 16.4-16.6 us against
+    // 15.1 us, and on the 512-token 8-head fp32 decode 8.3-8.4 us against 6.3-7.5
+    // us. Its tail (partial stores written through to memory, a wait for them, a
+    // counter round trip, the reads of the last workgroup) is three dependent
+    // memory round trips on every workgroup's critical path, while the merge
+    // kernel after the split kernel adds about 2 us to a step.
     const int forced_merge = opt ? opt->force_merge : FD_MERGE_AUTO;
     const bool fusable = page_size == 0 && splits <= fd::kFusedMaxSplits && slices <= fd::kFusedCounters &&
                          gt * hp <= fd::kFusedMaxHeads && (long long)gt * hp * splits <= fd::kFusedMaxRows;

@@ -633,28 +633,45 @@ __device__ __forceinline__ bool paged_item(const SplitArgs &a, WorkList &w, int 
 // ---------------------------------------------------------------- paged item loop
 // The items of a paged workgroup, each handed to item(args, slice, b, split).
 // One item per workgroup (paged_item) unless the launch is persistent
-// (a separate kernel instantiation, PERSIST): then grid
-// x is one workgroup per resident slot, and each numbers the items once (the
-// work list) and claims them in item order, largest first, from a counter at the
-// end of the workspace's counter block: claim q is head slice q % slices of list
-// item q / slices. The next claim is issued before the current item is streamed,
-// so its round trip is hidden; no workgroup ever waits for another, and a
-// workgroup that starts late simply claims less. A slot never idles waiting for
-// the dispatcher, and an XCD that streams slower takes fewer items. When the
-// claims run out each workgroup counts itself out on the next counter, and the
-// last one to leave sets both back to zero for the next call. Every thread of
-// the workgroup must call this (it holds barriers).
+// (a separate kernel instantiation, PERSIST): then grid x is one workgroup per
+// resident slot, and each numbers the items once (the work list) and takes
+// units in item order, largest first; unit q is head slice q % slices of list
+// item q / slices. Workgroup x starts with unit x without asking anyone; later
+// units are claimed from one counter (unit gridDim.x + claim), each claim
+// issued before the current unit is streamed so that its round trip is hidden.
+// No workgroup waits for another, a slot never idles waiting for the
+// dispatcher, and an XCD that streams slower takes fewer units. Same-address
+// device atomics serialize (about 11 ns apiece here), so no claim is made at
+// the start, when every workgroup would make one at once, and workgroups count
+// themselves out on one exit counter per XCD (x % kExitGroups); the last of a
+// group counts the group out, and the last group sets every counter back to
+// zero for the next call. Every thread of the workgroup must call this (it
+// holds barriers).
 // The kernel arguments as read back from an LDS copy for every item: the
 // compiler barrier before the read keeps the optimizer from hoisting anything
 // derived from them out of the item loop, and readfirstlane returns them to
-// scalar registers.
-__device__ __forceinline__ SplitArgs reload_args(const SplitArgs *s_args) {
+// scalar registers. The pointers are taken from the kernel argument itself,
+// which the compiler knows to address global memory: a pointer read back from
+// LDS is generic, every load through it becomes a flat load, and a flat load
+// also counts against the LDS wait counter, so each wait for an LDS access
+// would wait for every K/V load in flight as well.
+__device__ __forceinline__ SplitArgs reload_args(const SplitArgs &kern, const SplitArgs *s_args) {
     asm volatile("" ::: "memory");
     SplitArgs r;
     const int *src = reinterpret_cast<const int *>(s_args);
     int *dst = reinterpret_cast<int *>(&r);
 #pragma unroll
     for (int i = 0; i < (int)(sizeof(SplitArgs) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    r.q = kern.q;
+    r.k = kern.k;
+    r.v = kern.v;
+    r.block_table = kern.block_table;
+    r.seq_lens = kern.seq_lens;
+    r.ws_o = kern.ws_o;
+    r.ws_lse = kern.ws_lse;
+    r.out = kern.out;
+    r.err = kern.err;
+    r.counters = kern.counters;
     return r;
 }
 
@@ -667,28 +684,36 @@ __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
     } else {
         __shared__ int s_claim;
         __shared__ SplitArgs s_args;
-        unsigned *const claims = a.counters + kQueueCounter;
+        unsigned *const claims = a.counters + kQueueBase;          // units claimed past the first round
+        unsigned *const groups_done = claims + kQueueStride;       // exit groups whose workgroups are all gone
+        const int grp = (int)(blockIdx.x % kExitGroups);
+        unsigned *const gone = groups_done + (1 + grp) * kQueueStride;
         if (threadIdx.x == 0) s_args = a;
         const int total = build_work_list(a, s_list) * a.slices;
-        int claim = 0;  // thread 0: the claim in flight
-        if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
+        const bool claiming = total > (int)gridDim.x;  // else the first round holds every unit: no counter is used
+        int next = (int)blockIdx.x;  // thread 0: the next unit
         for (;;) {
-            if (threadIdx.x == 0) s_claim = claim;
+            if (threadIdx.x == 0) s_claim = next;
             __syncthreads();  // also ends every use of LDS by the previous item
             const int q = s_claim;
             __syncthreads();  // s_claim read by all before thread 0 writes the next one
             if (q >= total) break;
-            if (threadIdx.x == 0) claim = (int)atomicAdd(claims, 1u);
+            if (threadIdx.x == 0) next = claiming ? (int)gridDim.x + (int)atomicAdd(claims, 1u) : total;
             const int u = q / a.slices;
             int b, split;
             work_list_item(s_list, a.B, u, b, split);
-            item(reload_args(&s_args), q - u * a.slices, b, split);
+            item(reload_args(a, &s_args), q - u * a.slices, b, split);
         }
-        if (threadIdx.x == 0) {
-            const unsigned gone = atomicAdd(claims + 1, 1u) + 1u;
-            if (gone == gridDim.x) {  // every other workgroup has made its last claim
+        if (claiming && threadIdx.x == 0) {
+            const unsigned members = (gridDim.x - grp + kExitGroups - 1) / kExitGroups;
+            const unsigned groups = min(gridDim.x, (unsigned)kExitGroups);
+            if (atomicAdd(gone, 1u) + 1u == members && atomicAdd(groups_done, 1u) + 1u == groups) {
+                // every workgroup has made its last claim
                 __hip_atomic_store(claims, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(claims + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(groups_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int g = 0; g < kExitGroups; ++g)
+                    __hip_atomic_store(groups_done + (1 + g) * kQueueStride, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }

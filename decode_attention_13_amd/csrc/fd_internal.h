@@ -57,8 +57,13 @@ constexpr int kFusedMaxSplits = 32;
 constexpr int kFusedMaxHeads = 16;
 constexpr int kFusedMaxRows = 64;  // heads x splits one workgroup merges (4 x 32 or 16 x 4, ...)
 constexpr int kWsCounters = FD_WS_COUNTER_BYTES / 4;
-constexpr int kQueueCounter = kWsCounters - 2;  // persistent launch: next item to claim, then workgroups gone
-constexpr int kFusedCounters = kWsCounters - 2; // fused-merge counters available at the head of the block
+// Persistent launch, at the end of the block, each counter on a 256-byte line of
+// its own: the claim counter, the count of exit groups done, and one exit counter
+// per group of workgroups (blockIdx.x % kExitGroups, its XCD).
+constexpr int kExitGroups = 8;
+constexpr int kQueueStride = 64;  // words between two counters
+constexpr int kQueueBase = kWsCounters - (kExitGroups + 2) * kQueueStride;
+constexpr int kFusedCounters = kQueueBase;  // fused-merge counters available at the head of the block
 
 // Kinds of the debug error record.
 enum BadData { kBadTableEntry = 1, kBadSeqLen = 2 };

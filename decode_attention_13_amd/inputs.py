@@ -265,6 +265,18 @@ WORKLOADS = {
     ]
 }
 
+# Group sizes between MHA and the GQA4 batch, for the choice between the vector-ALU
+# and the matrix-core split kernels: the GQA4 batch's lengths and page size with 16
+# and 24 query heads on its 8 KV heads.
+CHOICE_WORKLOADS = {
+    w.name: w for w in [
+        PagedWorkload("paged_gqa2_bf16_b64_s1k-8k", 4, B=64, H=16, Hkv=8, D=128, dtype="bf16",
+                      page_size=16, len_kind="uniform", len_lo=1024, len_hi=8192),
+        PagedWorkload("paged_gqa3_bf16_b64_s1k-8k", 4, B=64, H=24, Hkv=8, D=128, dtype="bf16",
+                      page_size=16, len_kind="uniform", len_lo=1024, len_hi=8192),
+    ]
+}
+
 
 # --------------------------------------------------------------------------- prefill
 

@@ -589,6 +589,37 @@ def test_work_list_short_total_is_nan(device):
     assert torch.equal(o, outs[1])
 
 
+def test_persistent_counters_return_to_zero(device):
+    """Persistent launches of different sizes on one workspace (a KV-head group of 2
+    heads on one short sequence: 2 units; a 12-sequence batch; a 40-sequence batch),
+    repeated: each output is bit-identical to the one-item-per-workgroup grid, and
+    every claim and exit counter is back at zero after every call."""
+    cases = []
+    for B, H, Hkv, lens, seed in ((1, 8, 2, [100], 431), (12, 32, 8, None, 432), (40, 32, 8, None, 433)):
+        if lens is None:
+            lens = np.random.default_rng(seed).integers(0, 3000, B).tolist()
+        d = inputs.paged_inputs(B, H, Hkv, 128, "bf16", 16, lens, seed)
+        grid = fd.options(force_chunk=256, launch="grid")
+        g = to_dev(d, device)
+        ref = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                                 scale=d["scale"], max_seq_len=max(lens), total_kv=sum(lens), opt=grid).cpu()
+        cases.append((B, H, Hkv, lens, g, d, ref))
+    pers = fd.options(force_chunk=256, launch="persistent")
+    size = max(fd.paged_plan(B, H, Hkv, "bf16", 16, max(lens), sum(lens), 0, pers)["workspace_bytes"]
+               for B, H, Hkv, lens, _, _, _ in cases)
+    ws = fd.new_workspace(size, device)
+    for rep in range(3):
+        for B, H, Hkv, lens, g, d, ref in cases:
+            plan = fd.paged_plan(B, H, Hkv, "bf16", 16, max(lens), sum(lens), 0, pers)
+            assert plan["persistent"] == 1
+            announce(f"persistent counters rep {rep} B={B} grid_x={plan['grid_x']}")
+            o = fd.fd_paged_decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], 16,
+                                   scale=d["scale"], max_seq_len=max(lens), total_kv=sum(lens), opt=pers, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o.cpu(), ref), (rep, B)
+            assert torch.all(ws[:fd.binding.WS_COUNTER_BYTES] == 0), (rep, B)
+
+
 def test_workspace_too_small_is_rejected(device):
     d = to_dev(inputs.single_inputs(8, 8, 4096, 128, "bf16", 95), device)
     plan = fd.decode_plan(8, 8, 4096, "bf16", 0, fd.options(force_num_splits=4))
