@@ -499,10 +499,13 @@ __device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int
 struct WorkList {
     int full[kMaxListSeqs + 1];
     int rem[kMaxListSeqs];
-    int key[kMaxListSeqs];  // remainder size, 0 for an empty sequence, -1 for no remainder item
+    // remainder size, 0 for an empty sequence, -1 for no remainder item, -2 past the
+    // batch (below every real key, so it never outranks one)
+    __attribute__((aligned(16))) int key[kMaxListSeqs];
     int wave[kSplitThreads / 64];
     int rem_count;
 };
+static_assert(kMaxListSeqs == 4 * kSplitThreads, "the work list gives each thread 4 sequences");
 
 __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) {
     const int t = threadIdx.x;
@@ -514,16 +517,16 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
     for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
         const int bb = 4 * t + j;
         cnt[j] = 0;
-        key[j] = -1;
+        key[j] = -2;
         if (bb < a.B) {
             const int L = max(0, min(a.seq_lens[bb], a.max_len));
             cnt[j] = L / a.chunk;
             const int r = L - cnt[j] * a.chunk;
             key[j] = (r > 0 || L == 0) ? r : -1;
-            w.key[bb] = key[j];
         }
         local += cnt[j];
     }
+    *reinterpret_cast<int4 *>(&w.key[4 * t]) = make_int4(key[0], key[1], key[2], key[3]);
     int x = local;  // inclusive scan over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -542,12 +545,19 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
         excl += cnt[j];
     }
     if (t == kSplitThreads - 1) w.full[a.B] = excl;  // the last thread's end is the total
-    // Rank of each remainder item: items that are larger, or as large from an earlier sequence.
+    // Rank of each remainder item: items that are larger, or as large from an
+    // earlier sequence. Four keys per LDS read (every lane reads the same
+    // address: a broadcast); the keys past the batch are -2 and never count.
     int rank[4] = {0, 0, 0, 0};
-    for (int bb = 0; bb < a.B; ++bb) {
-        const int kb = w.key[bb];
+    const int4 *keys4 = reinterpret_cast<const int4 *>(w.key);
+    for (int i = 0; i < (a.B + 3) / 4; ++i) {
+        const int4 k4 = keys4[i];
+        const int kb[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rank[j] += (kb > key[j] || (kb == key[j] && bb < 4 * t + j)) ? 1 : 0;
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                rank[j] += (kb[e] > key[j] || (kb[e] == key[j] && 4 * i + e < 4 * t + j)) ? 1 : 0;
     }
     int mine = 0;
 #pragma unroll
@@ -637,12 +647,16 @@ __device__ __forceinline__ bool paged_item(const SplitArgs &a, WorkList &w, int 
 // resident slot, and each numbers the items once (the work list) and takes
 // units in item order, largest first; unit q is head slice q % slices of list
 // item q / slices. Workgroup x starts with unit x without asking anyone; later
-// units are claimed from one counter (unit gridDim.x + claim), each claim
-// issued before the current unit is streamed so that its round trip is hidden.
-// No workgroup waits for another, a slot never idles waiting for the
-// dispatcher, and an XCD that streams slower takes fewer units. Same-address
-// device atomics serialize (about 11 ns apiece here), so no claim is made at
-// the start, when every workgroup would make one at once, and workgroups count
+// units are claimed from one counter (unit gridDim.x + claim), each claim made
+// when the workgroup's current unit is done. No workgroup waits for another, a
+// slot never idles waiting for the dispatcher, and an XCD that streams slower
+// (the XCDs of this GPU differ by up to a third on the same batch) takes fewer
+// units. A claim made at the start of the unit before, to hide its round trip,
+// cost more than it saved: at the end of the launch the slots still holding
+// claimed units ran up to a whole unit past those that found the counter
+// empty (GQA4 batch: split kernel 206 us against 196 us). Same-address device
+// atomics serialize (about 11 ns apiece here), so no claim is made at the
+// start, when every workgroup would make one at once, and workgroups count
 // themselves out on one exit counter per XCD (x % kExitGroups); the last of a
 // group counts the group out, and the last group sets every counter back to
 // zero for the next call. Every thread of the workgroup must call this (it
@@ -698,11 +712,11 @@ __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
             const int q = s_claim;
             __syncthreads();  // s_claim read by all before thread 0 writes the next one
             if (q >= total) break;
-            if (threadIdx.x == 0) next = claiming ? (int)gridDim.x + (int)atomicAdd(claims, 1u) : total;
             const int u = q / a.slices;
             int b, split;
             work_list_item(s_list, a.B, u, b, split);
             item(reload_args(a, &s_args), q - u * a.slices, b, split);
+            if (threadIdx.x == 0) next = claiming ? (int)gridDim.x + (int)atomicAdd(claims, 1u) : total;
         }
         if (claiming && threadIdx.x == 0) {
             const unsigned members = (gridDim.x - grp + kExitGroups - 1) / kExitGroups;
