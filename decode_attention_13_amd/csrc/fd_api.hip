@@ -207,12 +207,20 @@ fd_status make_plan(int B, int H, int Hkv, fd_dtype dtype, int max_len, long lon
             if (uses_work_list(B, max_len, total, total_known, c)) chunk = c;
         }
     } else {
-        // Token-rows over all workgroups divided by the workgroups wanted,
-        // rounded down to a power of two, then clamped.
-        const long long work = std::max(total, 1LL) * slices;
+        // The splits that give the workgroups wanted (head slices x splits), then
+        // the tokens per split: S / splits rounded down to a multiple of 16, so
+        // that the fold gives exactly those splits and the last one holds fewer
+        // than 16 x splits extra tokens. A grid just past a multiple of the CUs
+        // would put two workgroups on a few CUs, whose halved bandwidth sets the
+        // kernel's time: 283264 tokens of a GQA4 cache in 34 power-of-two splits
+        // (272 workgroups) ran at 44% of peak, the same bytes on 256 workgroups
+        // at 76%. A coarser rounding (64) left 100000 tokens with a last split
+        // 1.55 times the others.
         const long long kv_bytes = std::max(total, 1LL) * Hkv * 2LL * FD_HEAD_DIM * cache_elem_bytes(dtype);
         const long long target = (long long)num_cus * target_wgs_per_cu(dtype, H == Hkv, kv_bytes);
-        chunk = pow2_floor(std::max(1LL, work / target));
+        const long long want = std::max(1LL, target / slices);
+        const long long per = std::max(1LL, std::max(total, 1LL) / want);
+        chunk = per / kMinChunk * kMinChunk;
         chunk = std::min<long long>(std::max<long long>(chunk, kMinChunk), kMaxChunk);
     }
     // A paged split spans at most chunk tokens, i.e. at most (chunk - 1) / page_size
