@@ -365,6 +365,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             pv(j & 1, p_cur);
             const Scores sc2 = scores(j & 1);
             rescale = softmax(sc1, p_next);
+            // Interleave the block for the scheduler: one MFMA, then three VALU
+            // instructions, for each MFMA of the block (left alone, the compiler
+            // bunched the softmax; this ordering ran the bf16 workload 3% and
+            // the f16 one 1.5% faster).
+            constexpr int kBlockMfma = QB * (8 + 8 * (M::kSplitP ? 2 : 1));
+#pragma unroll
+            for (int sg = 0; sg < kBlockMfma; ++sg) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+            }
             sc1 = sc2;
             p_cur = p_next;
         } else if (j < n_w) {
