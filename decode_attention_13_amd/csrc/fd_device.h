@@ -499,13 +499,18 @@ __device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int
 struct WorkList {
     int full[kMaxListSeqs + 1];
     int rem[kMaxListSeqs];
-    // remainder size, 0 for an empty sequence, -1 for no remainder item, -2 past the
-    // batch (below every real key, so it never outranks one)
+    // Sort key of sequence b's remainder item: its size (0 for an empty sequence)
+    // times kMaxListSeqs plus kMaxListSeqs - 1 - b, so that keys are distinct and
+    // a larger key is a larger item or an as large one of an earlier sequence;
+    // -1 for a sequence without a remainder item and past the batch.
     __attribute__((aligned(16))) int key[kMaxListSeqs];
     int wave[kSplitThreads / 64];
     int rem_count;
 };
 static_assert(kMaxListSeqs == 4 * kSplitThreads, "the work list gives each thread 4 sequences");
+// A remainder is shorter than a split, which spans at most kMaxSplitPages - 2
+// pages of at most 1024 tokens: its sort key fits an int.
+static_assert((long long)((kMaxSplitPages - 2) * 1024 + 1) * kMaxListSeqs < (1LL << 31), "sort keys overflow");
 
 __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) {
     const int t = threadIdx.x;
@@ -517,12 +522,12 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
     for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
         const int bb = 4 * t + j;
         cnt[j] = 0;
-        key[j] = -2;
+        key[j] = -1;
         if (bb < a.B) {
             const int L = max(0, min(a.seq_lens[bb], a.max_len));
             cnt[j] = L / a.chunk;
             const int r = L - cnt[j] * a.chunk;
-            key[j] = (r > 0 || L == 0) ? r : -1;
+            if (r > 0 || L == 0) key[j] = r * kMaxListSeqs + (kMaxListSeqs - 1 - bb);
         }
         local += cnt[j];
     }
@@ -545,26 +550,37 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
         excl += cnt[j];
     }
     if (t == kSplitThreads - 1) w.full[a.B] = excl;  // the last thread's end is the total
-    // Rank of each remainder item: items that are larger, or as large from an
-    // earlier sequence. Four keys per LDS read (every lane reads the same
-    // address: a broadcast); the keys past the batch are -2 and never count.
-    int rank[4] = {0, 0, 0, 0};
+    // Rank of each remainder item: the number of larger keys (larger items, or
+    // as large ones of earlier sequences), read four keys per LDS access (every
+    // lane reads the same address: a broadcast). Up to kSplitThreads sequences
+    // each thread ranks one (B compares), beyond that its four.
     const int4 *keys4 = reinterpret_cast<const int4 *>(w.key);
-    for (int i = 0; i < (a.B + 3) / 4; ++i) {
-        const int4 k4 = keys4[i];
-        const int kb[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                rank[j] += (kb[e] > key[j] || (kb[e] == key[j] && 4 * i + e < 4 * t + j)) ? 1 : 0;
-    }
+    const int n4 = (a.B + 3) / 4;
     int mine = 0;
+    if (a.B <= kSplitThreads) {  // (every key is in LDS since the scan's barrier)
+        const int k_me = t < a.B ? w.key[t] : -1;
+        if (k_me >= 0) {
+            int rank = 0;
+            for (int i = 0; i < n4; ++i) {
+                const int4 k4 = keys4[i];
+                rank += (k4.x > k_me) + (k4.y > k_me) + (k4.z > k_me) + (k4.w > k_me);
+            }
+            w.rem[rank] = t;
+            mine = 1;
+        }
+    } else {
+        int rank[4] = {0, 0, 0, 0};
+        for (int i = 0; i < n4; ++i) {
+            const int4 k4 = keys4[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (key[j] >= 0) {
-            w.rem[rank[j]] = 4 * t + j;
-            ++mine;
+            for (int j = 0; j < 4; ++j) rank[j] += (k4.x > key[j]) + (k4.y > key[j]) + (k4.z > key[j]) + (k4.w > key[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (key[j] >= 0) {
+                w.rem[rank[j]] = 4 * t + j;
+                ++mine;
+            }
         }
     }
     if (mine) atomicAdd(&w.rem_count, mine);
