@@ -494,8 +494,10 @@ __device__ __forceinline__ void check_paged_split(const SplitArgs &a, int b, int
 //
 // build_work_list fills s_full[b] = full splits of the sequences before b
 // (s_full[B] = F, their total) and s_rem[k] = the sequence of the k-th
-// remainder item, and returns the item count F + R. Every thread of the
-// workgroup must call this (it holds barriers). B <= kMaxListSeqs.
+// remainder item, and returns the item count F + R; it runs in two halves
+// (list_full_splits, list_remainders) because full-split items are found
+// from s_full alone. Every thread of the workgroup must call these (they hold
+// barriers). B <= kMaxListSeqs.
 struct WorkList {
     int full[kMaxListSeqs + 1];
     int rem[kMaxListSeqs];
@@ -505,6 +507,7 @@ struct WorkList {
     // -1 for a sequence without a remainder item and past the batch.
     __attribute__((aligned(16))) int key[kMaxListSeqs];
     int wave[kSplitThreads / 64];
+    int wave_rem[kSplitThreads / 64];
     int rem_count;
 };
 static_assert(kMaxListSeqs == 4 * kSplitThreads, "the work list gives each thread 4 sequences");
@@ -512,12 +515,14 @@ static_assert(kMaxListSeqs == 4 * kSplitThreads, "the work list gives each threa
 // pages of at most 1024 tokens: its sort key fits an int.
 static_assert((long long)((kMaxSplitPages - 2) * 1024 + 1) * kMaxListSeqs < (1LL << 31), "sort keys overflow");
 
-__device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) {
+// First half of the list: s_full and rem_count (the remainder items, R), from
+// the sequence lengths. Returns F. Every thread of the workgroup must call this
+// (it holds a barrier).
+__device__ __forceinline__ int list_full_splits(const SplitArgs &a, WorkList &w) {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    if (t == 0) w.rem_count = 0;
     int cnt[4], key[4];
-    int local = 0;
+    int local = 0, local_r = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // sequences 4t .. 4t + 3
         const int bb = 4 * t + j;
@@ -530,15 +535,23 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
             if (r > 0 || L == 0) key[j] = r * kMaxListSeqs + (kMaxListSeqs - 1 - bb);
         }
         local += cnt[j];
+        local_r += key[j] >= 0 ? 1 : 0;
     }
     *reinterpret_cast<int4 *>(&w.key[4 * t]) = make_int4(key[0], key[1], key[2], key[3]);
-    int x = local;  // inclusive scan over the wave
+    int x = local, xr = local_r;  // inclusive scans over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
+        const int yr = __shfl_up(xr, off, 64);
+        if (lane >= off) {
+            x += y;
+            xr += yr;
+        }
     }
-    if (lane == 63) w.wave[wave] = x;
+    if (lane == 63) {
+        w.wave[wave] = x;
+        w.wave_rem[wave] = xr;
+    }
     __syncthreads();
     int base = 0;
     for (int v = 0; v < wave; ++v) base += w.wave[v];
@@ -549,15 +562,27 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
         if (bb < a.B) w.full[bb] = excl;
         excl += cnt[j];
     }
-    if (t == kSplitThreads - 1) w.full[a.B] = excl;  // the last thread's end is the total
-    // Rank of each remainder item: the number of larger keys (larger items, or
-    // as large ones of earlier sequences), read four keys per LDS access (every
-    // lane reads the same address: a broadcast). Up to kSplitThreads sequences
-    // each thread ranks one (B compares), beyond that its four.
+    if (t == kSplitThreads - 1) {  // the last thread's ends are the totals
+        w.full[a.B] = excl;
+        int rtot = 0;
+        for (int v = 0; v < kSplitThreads / 64; ++v) rtot += w.wave_rem[v];
+        w.rem_count = rtot;
+    }
+    __syncthreads();
+    return w.full[a.B];
+}
+
+// Second half: s_rem, the remainder items in order. Rank of each: the number of
+// larger keys (larger items, or as large ones of earlier sequences), read four
+// keys per LDS access (every lane reads the same address: a broadcast). Up to
+// kSplitThreads sequences each thread ranks one (B compares), beyond that its
+// four. Every thread of the workgroup must call this, after list_full_splits
+// (it holds a barrier).
+__device__ __forceinline__ void list_remainders(const SplitArgs &a, WorkList &w) {
+    const int t = threadIdx.x;
     const int4 *keys4 = reinterpret_cast<const int4 *>(w.key);
     const int n4 = (a.B + 3) / 4;
-    int mine = 0;
-    if (a.B <= kSplitThreads) {  // (every key is in LDS since the scan's barrier)
+    if (a.B <= kSplitThreads) {
         const int k_me = t < a.B ? w.key[t] : -1;
         if (k_me >= 0) {
             int rank = 0;
@@ -566,9 +591,10 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
                 rank += (k4.x > k_me) + (k4.y > k_me) + (k4.z > k_me) + (k4.w > k_me);
             }
             w.rem[rank] = t;
-            mine = 1;
         }
     } else {
+        const int4 mine = keys4[t];
+        const int key[4] = {mine.x, mine.y, mine.z, mine.w};
         int rank[4] = {0, 0, 0, 0};
         for (int i = 0; i < n4; ++i) {
             const int4 k4 = keys4[i];
@@ -576,16 +602,17 @@ __device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) 
             for (int j = 0; j < 4; ++j) rank[j] += (k4.x > key[j]) + (k4.y > key[j]) + (k4.z > key[j]) + (k4.w > key[j]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (key[j] >= 0) {
-                w.rem[rank[j]] = 4 * t + j;
-                ++mine;
-            }
-        }
+        for (int j = 0; j < 4; ++j)
+            if (key[j] >= 0) w.rem[rank[j]] = 4 * t + j;
     }
-    if (mine) atomicAdd(&w.rem_count, mine);
     __syncthreads();
-    return w.full[a.B] + w.rem_count;
+}
+
+// The whole list; returns the item count F + R.
+__device__ __forceinline__ int build_work_list(const SplitArgs &a, WorkList &w) {
+    const int F = list_full_splits(a, w);
+    list_remainders(a, w);
+    return F + w.rem_count;
 }
 
 // The sequence of the r-th full split: the largest b with full[b] <= r. full
@@ -719,8 +746,13 @@ __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
         const int grp = (int)(blockIdx.x % kExitGroups);
         unsigned *const gone = groups_done + (1 + grp) * kQueueStride;
         if (threadIdx.x == 0) s_args = a;
-        const int total = build_work_list(a, s_list) * a.slices;
+        // The remainder items are ranked only when the first of them is taken:
+        // a workgroup whose first unit is a full split (on most batches all of
+        // them) starts streaming without waiting for the ranking.
+        const int F = list_full_splits(a, s_list);
+        const int total = (F + s_list.rem_count) * a.slices;
         const bool claiming = total > (int)gridDim.x;  // else the first round holds every unit: no counter is used
+        bool ranked = false;
         int next = (int)blockIdx.x;  // thread 0: the next unit
         for (;;) {
             if (threadIdx.x == 0) s_claim = next;
@@ -729,6 +761,10 @@ __device__ __forceinline__ void paged_items(const SplitArgs &a, ItemFn item) {
             __syncthreads();  // s_claim read by all before thread 0 writes the next one
             if (q >= total) break;
             const int u = q / a.slices;
+            if (u >= F && !ranked) {  // uniform over the workgroup
+                list_remainders(a, s_list);
+                ranked = true;
+            }
             int b, split;
             work_list_item(s_list, a.B, u, b, split);
             item(reload_args(a, &s_args), q - u * a.slices, b, split);
