@@ -141,11 +141,13 @@ typedef struct fd_plan {
                                total_kv is known */
     int persistent;         /* 1 (paged only): grid_x = one workgroup per resident slot (two per compute
                                unit), grid_y = grid_z = 1; every workgroup numbers the items as the work
-                               list does and claims them, largest first, from a counter in the
-                               workspace's counter block until none is left. Chosen when the item grid
-                               would take more than one round of resident workgroups (B <= 1024). The
-                               split stride, the splits and so the results are those of the grid form;
-                               total_kv only sizes the splits (every item is processed). */
+                               list does (units = items x head slices, largest first), starts with its
+                               own unit (workgroup x takes unit x) and, each time a unit is done,
+                               claims the next from a counter in the workspace's counter block until
+                               none is left. Chosen when the units would take more than one round of
+                               resident workgroups (B <= 1024). The split stride, the splits and so
+                               the results are those of the grid form; total_kv only sizes the
+                               splits (every item is processed). */
     size_t ws_err_offset;   /* paged plans with debug_checks: byte offset of the 16-byte error
                                record (int32 kind, sequence, table index or 0, offending value;
                                kind 1 = table entry, 2 = sequence length) inside the workspace,
@@ -159,11 +161,13 @@ typedef struct fd_plan {
 /*
  * Workspace layout when merge != 0 (every plan uses the same head block, so one
  * workspace serves calls of any plan):
- *   counters [FD_WS_COUNTER_BYTES / 4] uint32 at byte 0: a fused launch counts
- *                                the finished splits of each (sequence, head
- *                                slice) from the start of the block, a
- *                                persistent launch its claims in the last two
- *                                words. They must be ZERO before the workspace
+ *   counters [FD_WS_COUNTER_BYTES / 4] uint32 at byte 0: a fused launch
+ *                                (contiguous cache) counts the finished splits
+ *                                of each head slice from the start of the
+ *                                block, a persistent launch its claims and its
+ *                                finished workgroups in the last 640 words
+ *                                (10 counters, 256 bytes apart). They must be
+ *                                ZERO before the workspace
  *                                is first used (e.g. hipMemset once after
  *                                allocating it); every completed call leaves
  *                                them zero. A persistent plan needs this block
