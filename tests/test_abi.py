@@ -330,6 +330,24 @@ def test_debug_record_in_the_paged_plan():
                                                                          fd.options(debug_checks=1))
 
 
+def test_contiguous_plan_fills_the_cus_exactly():
+    """Contiguous caches: the split count comes from the workgroups wanted (one per
+    CU here) and the chunk is S / splits rounded down to 16 tokens, so the grid is
+    a whole multiple of the CUs and the last split, which takes the remainder,
+    holds fewer than 16 x splits extra tokens; power-of-two lengths keep their
+    power-of-two chunks."""
+    for H, Hkv, S in ((32, 8, 283264), (32, 8, 100000), (32, 32, 99991), (64, 8, 50000), (32, 32, 131073)):
+        p = fd.decode_plan(H, Hkv, S, "bf16", 256)
+        wgs = p["grid_x"] * p["grid_y"]
+        assert wgs == 256, (H, Hkv, S, p)
+        assert p["chunk"] % 16 == 0 and p["num_splits"] == S // p["chunk"]
+        last = S - (p["num_splits"] - 1) * p["chunk"]
+        assert p["chunk"] <= last < p["chunk"] + 16 * p["num_splits"], (S, p["chunk"], last)
+    assert fd.decode_plan(32, 32, 4096, "bf16", 256)["chunk"] == 256
+    assert fd.decode_plan(32, 32, 131072, "bf16", 256)["chunk"] == 8192
+    assert fd.decode_plan(8, 8, 512, "f32", 256)["chunk"] == 16
+
+
 def test_merge_choice():
     """Multi-split plans merge with the merge kernel unless the fused merge (the last
     workgroups merge, one launch) is asked for; it is available for a contiguous cache
