@@ -73,7 +73,7 @@ typedef enum fd_status {
 enum {
     FD_MERGE_AUTO = 0,   /* planner's choice */
     FD_MERGE_KERNEL = 1, /* a second kernel merges the split partials */
-    FD_MERGE_FUSED = 2   /* the last workgroup of each (sequence, head slice) merges them: one launch */
+    FD_MERGE_FUSED = 2   /* contiguous caches: the last workgroup of each head slice merges them: one launch */
 };
 
 enum {
@@ -128,8 +128,8 @@ typedef struct fd_plan {
                                    and persistent */
     int threads;         /* split kernel workgroup size */
     int merge;           /* 0: one split per sequence, o written directly; 1 (FD_MERGE_KERNEL): partials
-                            go to the workspace and a merge kernel runs; 2 (FD_MERGE_FUSED): one launch, the
-                            last workgroup of each (sequence, head slice) merges its partials */
+                            go to the workspace and a merge kernel runs; 2 (FD_MERGE_FUSED, contiguous caches
+                            only): one launch, the last workgroup of each head slice merges its partials */
     int kv_heads_per_group; /* adjacent KV heads one workgroup reads together (vector-ALU kernel with
                                H == Hkv: 2, or 4 for an E4M3 cache; else 1) */
     size_t workspace_bytes; /* bytes the workspace must hold (0 when merge == 0 and no debug record) */
