@@ -12,7 +12,7 @@ throughput on a bounded sample of the same workload and, for single-sequence
 decode workloads, the KV-length curve the metric is stated over (32 heads,
 S = 4k .. 128k and 131073 tokens; "sweep").
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--no-sweep] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv fp8] [--no-sweep] [--no-cpu-baseline] [--graph]
   python bench.py --workload prefill_bf16_h32_n4096_causal   # the prefill kernel (TFLOP/s, matrix-core roofline)
   python bench.py --copy-probe BYTES   # a plain device copy, to scale rocprof byte counters
 """
@@ -128,9 +128,10 @@ class Case:
         self.stream = torch.cuda.current_stream()
         log(f"{w.name}: plan {self.plan}, {self.copies} KV copies of {self.kv_bytes / 1e6:.1f} MB")
 
-    def step(self, i: int, opt=None) -> None:
+    def step(self, i: int, opt=None, stream=None) -> None:
         import ctypes
         k, v = self.kv[i % self.copies]
+        st = self.stream.cuda_stream if stream is None else stream.cuda_stream
         o = opt if opt is not None else self.opt
         optp = ctypes.byref(o) if o is not None else None
         w = self.w
@@ -138,24 +139,24 @@ class Case:
             rc = self.lib.fd_decode_fp8kv(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), w.H, w.Hkv,
                                           w.S, 128, self.dtype_code, self.d["scale"], self.d["k_scale"],
                                           self.d["v_scale"], self.ws.data_ptr(), self.ws.numel(), optp,
-                                          self.stream.cuda_stream)
+                                          st)
         elif w.kind == "single":
             rc = self.lib.fd_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.o.data_ptr(), w.H, w.Hkv, w.S,
                                     128, self.dtype_code, self.d["scale"], self.ws.data_ptr(),
-                                    self.ws.numel(), optp, self.stream.cuda_stream)
+                                    self.ws.numel(), optp, st)
         elif self.fp8:
             rc = self.lib.fd_paged_decode_fp8kv(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.table.data_ptr(),
                                                 self.lens.data_ptr(), w.page_size, self.o.data_ptr(), self.d["scale"],
                                                 self.d["k_scale"], self.d["v_scale"], w.B, w.H, w.Hkv, 128,
                                                 self.d["num_pages"], self.d["max_blocks"], self.d["max_seq_len"],
                                                 self.total, self.dtype_code, self.ws.data_ptr(), self.ws.numel(),
-                                                optp, self.stream.cuda_stream)
+                                                optp, st)
         else:
             rc = self.lib.fd_paged_decode(self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.table.data_ptr(),
                                           self.lens.data_ptr(), w.page_size, self.o.data_ptr(), self.d["scale"], w.B,
                                           w.H, w.Hkv, 128, self.d["num_pages"], self.d["max_blocks"],
                                           self.d["max_seq_len"], self.total, self.dtype_code, self.ws.data_ptr(),
-                                          self.ws.numel(), optp, self.stream.cuda_stream)
+                                          self.ws.numel(), optp, st)
         if rc != 0:
             raise RuntimeError(f"{self.lib.fd_status_string(rc).decode()}: {self.lib.fd_last_error().decode()}")
 
@@ -163,6 +164,30 @@ class Case:
 def inputs_dtype(name: str):
     from decode_attention_13_amd.inputs import DTYPES
     return DTYPES[name]
+
+
+def time_graph(case: Case, steps: int) -> dict:
+    """The step captured in a HIP graph (torch.cuda.graph): one captured step per
+    rotated KV copy, the graph replayed back to back; wall time per step."""
+    import torch
+
+    n = case.copies
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for i in range(n):
+            case.step(i, stream=cap)
+    reps = max(1, steps // n)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return {"us_per_step": round((time.perf_counter() - t0) / (reps * n) * 1e6, 3), "steps": reps * n,
+            "steps_per_replay": n}
 
 
 def time_steps(case: Case, steps: int, warmup: int) -> dict:
@@ -455,6 +480,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the pages' KV-length sweep (4k..128k) also for a paged workload")
     ap.add_argument("--no-sweep", action="store_true", help="skip the KV-length sweep")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (field \"graph\")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
@@ -510,6 +537,9 @@ def main() -> int:
                      "bytes_per_launch": case.kv_bytes,
                      "bytes_per_unit": case.kv_bytes // case.units, "units_per_launch": case.units},
     }
+    if args.graph:
+        line["graph"] = time_graph(case, args.steps)
+        log(f"graph replay: {line['graph']}")
     case_fp8 = case.fp8
     del case
     torch.cuda.empty_cache()
