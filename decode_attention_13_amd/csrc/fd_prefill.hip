@@ -10,9 +10,9 @@
 // own workgroup, waves split by query rows) is kept.
 //
 // Workgroup: 4 waves x 16 * QB queries of one (sequence, head); key tiles of 32
-// tokens staged in LDS (two K and two V buffers) and shared by the 4 waves.
-// Per wave, 16-query block and tile, the matrix-core work is that of the decode
-// kernel with query rows in place of query heads:
+// tokens shared by the 4 waves. Per wave, 16-query block and tile, the
+// matrix-core work is that of the decode kernel with query rows in place of
+// query heads:
 //   S^T[key, q] = K[key, :] . Q[q, :]       two 16x16x32 MFMA chains of 4
 //   online softmax per query (column), log2 domain, fp32
 //   O^T[d, q] += V^T[d, key] . P^T[key, q]  eight 16x16x32 MFMAs (bf16: P split
@@ -22,6 +22,14 @@
 // P^T needs no lane movement (key slot (l/16)*8 + j holds key
 // (j/4)*16 + (l/16)*4 + j%4, the keys of that lane's S accumulators); V^T comes
 // from the LDS tile with ds_read_b64_tr_b16.
+//
+// K and V tiles go from global memory straight into LDS (global_load_lds,
+// 16 bytes a lane, no registers on the way) through rings of four tiles each,
+// so a tile is requested three iterations before it is read: the loads meet
+// the latency of L2 and HBM without holding the loop. A tile is 32 unpadded
+// 256-byte rows; 16-byte chunk x of row r is stored at chunk x ^ (r % 16), so
+// the K fragment reads (16 rows, one chunk) and the transposed V reads (4 rows,
+// 2 chunks, per 16 lanes) both spread over all banks.
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -32,9 +40,10 @@ namespace {
 constexpr int kWaves = 4;      // waves per workgroup, 16 * QB queries each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKTile = 32;     // keys per LDS tile
-constexpr int kPieces = kKTile * 16 / kThreads;  // 16-byte pieces (16 per 256-B row) of a tile per thread
-constexpr int kKPad = 272;     // LDS bytes per K row (256 + 16)
-constexpr int kVPad = 288;     // LDS bytes per V row (256 + 32, as for the transposed reads)
+constexpr int kRow = 256;      // bytes of a K or V row in LDS (128 16-bit elements)
+constexpr int kTileBytes = kKTile * kRow;
+constexpr int kRing = 4;       // LDS tiles per ring (K and V each)
+constexpr int kDmaPerTile = kTileBytes / (kThreads * 16);  // 16-byte loads per lane and tile
 constexpr int kXcds = 8;       // XCDs of the MI355X, each with its own L2
 constexpr float kLazyLog2 = 8.f;  // the running max trails the true one by at most this (log2 units)
 
@@ -48,7 +57,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ float max2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): -inf and finite inputs as
+// usual, NaN propagates; unlike maxnum it needs no canonicalisation of the MFMA
+// results it reads.
+__device__ __forceinline__ float max2(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
 template <typename T>
 struct Mma;
@@ -63,8 +75,14 @@ struct Mma<__bf16> {
     __device__ static uint32_t pack2(float x, float y) {
         return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
     }
-    __device__ static float lo_of(uint32_t w) { return bf16_lo(w); }
-    __device__ static float hi_of(uint32_t w) { return bf16_hi(w); }
+    // x = hi + lo: hi is x truncated to bf16 (its upper 16 bits, packed for two
+    // values by one byte permute), lo the exact remainder x - hi rounded to
+    // bf16, so hi + lo keeps 16 significant bits of x.
+    __device__ static void split2(float x, float y, uint32_t &hi, uint32_t &lo) {
+        const uint32_t xb = __builtin_bit_cast(uint32_t, x), yb = __builtin_bit_cast(uint32_t, y);
+        hi = __builtin_amdgcn_perm(yb, xb, 0x07060302u);  // (y & 0xffff0000) | (x >> 16)
+        lo = pack2(x - __builtin_bit_cast(float, xb & 0xffff0000u), y - __builtin_bit_cast(float, yb & 0xffff0000u));
+    }
 };
 
 template <>
@@ -74,12 +92,32 @@ struct Mma<_Float16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                       0, 0, 0);
     }
-    __device__ static uint32_t pack2(float x, float y) {
-        return __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
+    __device__ static void split2(float x, float y, uint32_t &hi, uint32_t &lo) {
+        hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
+        lo = 0;
     }
-    __device__ static float lo_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
-    __device__ static float hi_of(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
 };
+
+// One 16-byte global load per lane written straight to LDS: lane l's bytes go
+// to LDS address lds + 16 * l (lds wave-uniform, passed in m0). Written as
+// inline assembly so that the compiler, which would otherwise wait for every
+// such load before any later LDS read, leaves the waits to wait_vm below; the
+// instruction has no register result. m0 is set one instruction ahead of its
+// use, as the LDS-load form requires.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter alone (expcnt and lgkmcnt left free):
+// wait until at most N loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xf << 8) | (0x7 << 4) | (N & 0xf));
+}
 
 // QB: blocks of 16 queries per wave. Every K and V fragment read from LDS
 // feeds QB MFMA column blocks, so LDS traffic per flop falls as 1 / QB.
@@ -121,70 +159,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int kv_end = a.causal ? min(N, (qt + 1) * kQTile) : N;
     const int ntiles = (kv_end + kKTile - 1) / kKTile;
 
-    __shared__ __attribute__((aligned(16))) char sK[2][kKTile * kKPad];
-    __shared__ __attribute__((aligned(16))) char sV[2][kKTile * kVPad];
+    __shared__ __attribute__((aligned(16))) char sK[kRing][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char sV[kRing][kTileBytes];
 
-    // Q fragments (B operand of S): query q0 + 16*qb + c, head-dim slots kk*32 + g*8 .. +8.
-    uint4 qf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qr = min(q0 + 16 * qb + c, N - 1);
-        const T *qrow = reinterpret_cast<const T *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = load16(qrow + kk * 32 + g * 8);
-    }
-    // A negative scale is moved into Q (a sign flip is exact), so the running
-    // max can be taken over the raw scores and scaled afterwards.
+    uint4 qf[QB][4];  // the wave's queries, loaded with the first tiles below
     // sl > 0 (a zero scale arrives as the least normal float), so -inf * sl
     // stays -inf and a masked score gives exp2 = 0.
     const float sl = fabsf(a.scale_log2);
-    if (a.scale_log2 < 0.f) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                qf[qb][kk].x ^= 0x80008000u;
-                qf[qb][kk].y ^= 0x80008000u;
-                qf[qb][kk].z ^= 0x80008000u;
-                qf[qb][kk].w ^= 0x80008000u;
-            }
-    }
 
-    // Tile staging: thread t moves 16-byte pieces t + i * kThreads of a K or V tile
-    // (piece p: row p / 16, bytes (p % 16) * 16); rows past N re-read row N - 1.
+    // Tile loads: load i of a wave fills 1 KB of the tile, rows 4 * (kDmaPerTile *
+    // wave + i) .. + 3, lane l the 16 bytes at l * 16 (row + l / 16, stored
+    // chunk l % 16), which hold chunk (l % 16) ^ (row % 16) of that key's row.
+    // Keys past N re-read key N - 1 (never used: masked, or past the workgroup).
     const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
     const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
     const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
-    // A whole tile: a wave-uniform tile base plus a fixed 32-bit offset per lane.
-    uint32_t lane_off[kPieces];
+    int dma_row[kDmaPerTile];
+    uint32_t dma_col[kDmaPerTile];
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-        const int p = threadIdx.x + i * kThreads;
-        lane_off[i] = (uint32_t)(p >> 4) * (uint32_t)tok_bytes + (p & 15) * 16;
+    for (int i = 0; i < kDmaPerTile; ++i) {
+        dma_row[i] = 4 * (kDmaPerTile * wave + i) + (lane >> 4);
+        dma_col[i] = (uint32_t)(((lane & 15) ^ (dma_row[i] & 15)) * 16);
     }
-    auto fetch = [&](const char *src, int j, uint4 (&st)[kPieces]) {
-        if (j * kKTile + kKTile <= N) {
-            // buffer loads from the uniform tile base (2% on the f16 GQA workload)
-            const __amdgpu_buffer_rsrc_t r = stream_rsrc(src + (size_t)j * kKTile * tok_bytes);
+    auto dma = [&](const char *src, char (*ring)[kTileBytes], int t) {
+        char *dst = ring[t & (kRing - 1)];
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off[i], 0, 0);
-                st[i] = make_uint4(x.x, x.y, x.z, x.w);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const int p = threadIdx.x + i * kThreads;
-                const int key = min(j * kKTile + (p >> 4), N - 1);
-                st[i] = load16(src + (size_t)key * tok_bytes + (p & 15) * 16);
-            }
-        }
-    };
-    auto put = [&](char *dst, int pad, const uint4 (&st)[kPieces]) {
-#pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int p = threadIdx.x + i * kThreads;
-            *(lds_u32x4 *)(uintptr_t)(dst + (p >> 4) * pad + (p & 15) * 16) = u32x4{st[i].x, st[i].y, st[i].z, st[i].w};
+        for (int i = 0; i < kDmaPerTile; ++i) {
+            const int key = min(t * kKTile + dma_row[i], N - 1);
+            const char *p = src + (size_t)key * tok_bytes + dma_col[i];
+            dma16(p, (uint32_t)(uintptr_t)(dst + (kDmaPerTile * wave + i) * 1024));
         }
     };
 
@@ -201,9 +204,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     struct Scores {
         f32x4 v[QB][2];
     };
-    // S^T of one tile from the K buffer.
-    auto scores = [&](int kbuf) {
-        lds_char *kt = (lds_char *)(uintptr_t)sK[kbuf];
+    // S^T of tile t from the K ring: lane (g, c) reads key row sb * 16 + c,
+    // chunk kk * 4 + g, stored at chunk (kk * 4 + g) ^ c.
+    auto scores = [&](int t) {
+        lds_char *kt = (lds_char *)(uintptr_t)sK[t & (kRing - 1)];
         Scores r;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int qb = 0; qb < QB; ++qb) r.v[qb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const u32x4 kr = *(lds_u32x4 *)(kt + (sb * 16 + c) * kKPad + kk * 64 + g * 16);
+                const u32x4 kr = *(lds_u32x4 *)(kt + (sb * 16 + c) * kRow + (((kk * 4 + g) ^ c) << 4));
                 const uint4 ka = make_uint4(kr.x, kr.y, kr.z, kr.w);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) r.v[qb][sb] = M::mma(ka, qf[qb][kk], r.v[qb][sb]);
@@ -251,8 +255,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const f32x4 s0 = sc.v[qb][0], s1 = sc.v[qb][1];
-            // Raw-score max (the scale is > 0: its sign was moved into Q); med3
-            // with +inf is a max that needs no NaN canonicalisation of its inputs.
+            // Raw-score max (the scale is > 0: its sign was moved into Q).
             float mt = max2(max2(max2(s0[0], s0[1]), max2(s0[2], s0[3])), max2(max2(s1[0], s1[1]), max2(s1[2], s1[3])));
             LanePair lp = lane_pair<16>(mt);
             mt = max2(lp.lo, lp.hi);
@@ -277,11 +280,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             lsum[qb] = __builtin_fmaf(lsum[qb], alpha[qb], ps);
             uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                hw[e2] = M::pack2(pe[2 * e2], pe[2 * e2 + 1]);
-                if constexpr (M::kSplitP)
-                    lw[e2] = M::pack2(pe[2 * e2] - M::lo_of(hw[e2]), pe[2 * e2 + 1] - M::hi_of(hw[e2]));
-            }
+            for (int e2 = 0; e2 < 4; ++e2) M::split2(pe[2 * e2], pe[2 * e2 + 1], hw[e2], lw[e2]);
             pr.hi[qb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             if constexpr (M::kSplitP) pr.lo[qb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
@@ -294,17 +293,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int db = 0; db < 8; ++db) acc[qb][db] *= alpha[qb];
     };
 
-    // O^T += V^T . P^T from a V buffer.
-    auto pv = [&](int vbuf, const Probs &pr) {
-        lds_char *vt = (lds_char *)(uintptr_t)sV[vbuf];
+    // O^T += V^T . P^T for tile t from the V ring: lane (g, c) reads 8 bytes of
+    // key rows g*4 + c/4 and 16 + g*4 + c/4 (columns db*16 + (c%4)*4 .. + 3:
+    // chunk db*2 + (c%4)/2, stored at that chunk ^ (g*4 + c/4)), transposed.
+    auto pv = [&](int t, const Probs &pr) {
+        lds_char *vt = (lds_char *)(uintptr_t)sV[t & (kRing - 1)];
         const int e = c >> 2, bq = c & 3;
+        const int rl = g * 4 + e;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const int col_bytes = (db * 16 + bq * 4) * 2;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(vt + (g * 4 + e) * kVPad + col_bytes));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(vt + (16 + g * 4 + e) * kVPad + col_bytes));
+            const int off = (((db * 2 + (bq >> 1)) ^ rl) << 4) + (bq & 1) * 8;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vt + rl * kRow + off));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vt + (16 + rl) * kRow + off));
             const u32x2v lo2 = __builtin_bit_cast(u32x2v, lo);
             const u32x2v hi2 = __builtin_bit_cast(u32x2v, hi);
             const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
@@ -318,41 +318,67 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
     // Software pipeline, three tiles deep: iteration j runs P.V of tile j and the
     // scores of tile j + 2 on the matrix cores while the VALU takes the softmax
-    // of tile j + 1 (none of the three waits for another). K runs two tiles ahead
-    // of V: iteration j fetches K(j + 3) and V(j + 1) from global memory and
-    // stores them, after its own LDS reads, into the buffers that iteration
-    // j - 1 finished reading; one barrier per tile.
+    // of tile j + 1 (none of the three waits for another). Iteration j requests
+    // K(j + 5) and V(j + 3) into the ring slots that iteration j - 1 finished
+    // reading, then waits for K(j + 3) and V(j + 1) (requested two iterations
+    // earlier; the 8 loads of the two later iterations may still be in flight)
+    // and meets the other waves at one barrier. Every iteration requests its
+    // tiles, past the end too (they re-read key N - 1 and are never read), so
+    // the count of loads in flight is the same on every iteration; the tiles
+    // requested past the end are the last loads to wait for.
     // Tiles this wave computes: with the causal mask those after its last query
-    // are skipped (the workgroup still stages them for its other waves). Scores
-    // formed past a wave's last tile read whatever the K buffer holds and are
+    // are skipped (the workgroup still loads them for its other waves). Scores
+    // formed past a wave's last tile read whatever the K ring holds and are
     // never used.
+    static_assert(kDmaPerTile == 2, "the waits below count 4 loads per iteration");
     const int n_w = a.causal ? min(ntiles, q_last / kKTile + 1) : ntiles;
     auto masked = [&](int j) { return j * kKTile + kKTile > N || (a.causal && j * kKTile + kKTile - 1 > q0); };
-    uint4 kst[kPieces], vst[kPieces], k2st[kPieces];
-    fetch(kg, 0, kst);
-    fetch(vg, 0, vst);
-    if (ntiles > 2) fetch(kg, 2, k2st);
-    put(sK[0], kKPad, kst);
-    put(sV[0], kVPad, vst);
-    if (ntiles > 1) {
-        fetch(kg, 1, kst);
-        put(sK[1], kKPad, kst);
+    // The first tiles, in the order they are needed: K0 K1 V0 K2, then the
+    // query rows, one wait for all of them (so the waits the compiler places for
+    // the queries count every load in flight), then V1 K3 V2; K4 shares its ring
+    // slot with K0 and follows the barrier after K0 is read.
+    dma(kg, sK, 0);
+    dma(kg, sK, 1);
+    dma(vg, sV, 0);
+    dma(kg, sK, 2);
+    // Q fragments (B operand of S): query q0 + 16*qb + c, head-dim slots kk*32 + g*8 .. +8.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qr = min(q0 + 16 * qb + c, N - 1);
+        const T *qrow = reinterpret_cast<const T *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = load16(qrow + kk * 32 + g * 8);
     }
-    __syncthreads();
+    // A negative scale is moved into Q (a sign flip is exact), so the running
+    // max can be taken over the raw scores and scaled afterwards.
+    if (a.scale_log2 < 0.f) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                qf[qb][kk].x ^= 0x80008000u;
+                qf[qb][kk].y ^= 0x80008000u;
+                qf[qb][kk].z ^= 0x80008000u;
+                qf[qb][kk].w ^= 0x80008000u;
+            }
+    }
+
+    wait_vm<0>();
+    dma(vg, sV, 1);
+    dma(kg, sK, 3);
+    dma(vg, sV, 2);
+    __builtin_amdgcn_s_barrier();
     Scores sc0 = scores(0);
     Scores sc1 = scores(1);  // tile 1, or discarded
-    __syncthreads();         // every wave has read K buffer 0
-    if (ntiles > 2) put(sK[0], kKPad, k2st);
     if (masked(0)) mask_scores(0, sc0);
     Probs p_cur;
-    softmax(sc0, p_cur);  // m starts at -inf: nothing to rescale
+    softmax(sc0, p_cur);   // m starts at -inf: nothing to rescale
     bool rescale = false;  // alpha of the last softmax applies before the next P.V
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();  // every wave has read K0 and K1
+    dma(kg, sK, 4);
     for (int j = 0; j < ntiles; ++j) {
-        const bool more_k = j + 3 < ntiles;
-        const bool more_v = j + 1 < ntiles;
-        if (more_k) fetch(kg, j + 3, kst);
-        if (more_v) fetch(vg, j + 1, vst);
+        dma(kg, sK, j + 5);
+        dma(vg, sV, j + 3);
         if (rescale) {  // softmax(j) moved m: before P.V(j)
             rescale_acc();
             rescale = false;
@@ -362,13 +388,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             Probs p_next;
             // One block for the scheduler: P.V(j) and scores(j + 2) on the matrix
             // cores, softmax(j + 1) on the VALU.
-            pv(j & 1, p_cur);
-            const Scores sc2 = scores(j & 1);
+            pv(j, p_cur);
+            const Scores sc2 = scores(j + 2);
             rescale = softmax(sc1, p_next);
             // Interleave the block for the scheduler: one MFMA, then three VALU
             // instructions, for each MFMA of the block (left alone, the compiler
-            // bunched the softmax; this ordering ran the bf16 workload 3% and
-            // the f16 one 1.5% faster).
+            // bunched the softmax).
             constexpr int kBlockMfma = QB * (8 + 8 * (M::kSplitP ? 2 : 1));
 #pragma unroll
             for (int sg = 0; sg < kBlockMfma; ++sg) {
@@ -378,12 +403,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             sc1 = sc2;
             p_cur = p_next;
         } else if (j < n_w) {
-            pv(j & 1, p_cur);
+            pv(j, p_cur);
         }
-        if (more_k) put(sK[(j + 1) & 1], kKPad, kst);
-        if (more_v) put(sV[(j + 1) & 1], kVPad, vst);
-        __syncthreads();
+        wait_vm<8>();  // K(j + 3) and V(j + 1)
+        __builtin_amdgcn_s_barrier();
     }
+
+    wait_vm<0>();  // no load may still be writing LDS when the workgroup ends
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {

@@ -68,12 +68,45 @@ def test_lengths(N, device):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_first_row_is_exact(dtype, device):
-    """Causal row 0 sees one key: o = v_0 of its KV head, bit for bit."""
+    """Causal row 0 sees one key: o = v_0 of its KV head, bit for bit (bf16 V
+    goes through f16, exact for 2^-17 <= |v| < 65536; the seeded row has no
+    smaller nonzero magnitude)."""
     d = inputs.prefill_inputs(2, 130, 6, 3, 128, dtype, 520)
+    v0 = d["v"][:, 0].to(torch.float32).abs()
+    assert not ((v0 > 0) & (v0 < 2.0 ** -17)).any()
     announce(f"first row {dtype}")
     o = run(d, device, True)
     want = d["v"][:, 0].repeat_interleave(2, dim=1)
     assert torch.equal(o[:, 0], want)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_tiles_beyond_f16(causal, device):
+    """bf16 V tiles holding magnitudes f16 cannot (|v| >= 65536, up to 1e30) stay
+    bf16 with P split in two parts; the tiles between them go through f16. Key
+    rows of tiles 1, 2 and 5 (staged by different waves) carry such values, so
+    P.V meets every pairing of the two formats in consecutive tiles; 65280, the
+    largest bf16 below 65536, and 65536 itself sit in tiles 3 and 6.
+
+    Outputs here can be small sums of terms near 1e4 that cancel, so the bound
+    also carries the conditioning of each output: P is kept to a relative 2^-12
+    or better (f16 P on f16 tiles; hi + lo, 2^-15, on bf16 tiles), which moves
+    o[d] by at most 2^-12 * sum_k w_k |v_k[d]|, the oracle's output for |V|."""
+    d = inputs.prefill_inputs(2, 200, 8, 2, 128, "bf16", 530)
+    v = d["v"].to(torch.float32)
+    for key, mult in [(32 + 3, 3e5), (64 + 21, -7e4), (160 + 30, 1e30), (160 + 9, 2e5)]:
+        v[:, key] *= mult
+    v[0, 96 + 12, 1, 5] = 65280.0
+    v[1, 192 + 4, 0, 77] = -65536.0
+    d["v"] = v.to(torch.bfloat16)
+    assert d["v"][0, 96 + 12, 1, 5].item() == 65280.0
+    announce(f"bf16 tiles beyond f16, causal={causal}")
+    o = run(d, device, causal)
+    ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
+    cond, _ = oracle.prefill_attention(d["q"], d["k"], d["v"].abs(), d["scale"], causal)
+    err = np.abs(o.to(torch.float64).numpy() - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref) + 2.0 ** -12 * cond)
+    assert not bad.any(), f"wide V causal={causal}: {int(bad.sum())} outside, max|err| {err.max():.3e}"
 
 
 def test_workload_prefill_bf16_h32_n4096_causal(device):
