@@ -110,6 +110,13 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
                  : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
+// The same load from a wave-uniform base (in SGPRs) plus a 32-bit lane offset.
+__device__ __forceinline__ void dma16_at(const void *sbase, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
 
 // s_waitcnt on the vector-memory counter alone (expcnt and lgkmcnt left free):
 // wait until at most N loads of this wave are in flight.
@@ -174,20 +181,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
     const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
     const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
+    // Lane offsets within a tile (row * token bytes + chunk; 32 rows of at most
+    // 65535 * 256 bytes fit in 32 bits): a tile wholly below N is one scalar base
+    // plus these, with no per-lane address arithmetic; a tile reaching past N
+    // clamps its keys lane by lane.
     int dma_row[kDmaPerTile];
-    uint32_t dma_col[kDmaPerTile];
+    uint32_t dma_col[kDmaPerTile], dma_off[kDmaPerTile];
 #pragma unroll
     for (int i = 0; i < kDmaPerTile; ++i) {
         dma_row[i] = 4 * (kDmaPerTile * wave + i) + (lane >> 4);
         dma_col[i] = (uint32_t)(((lane & 15) ^ (dma_row[i] & 15)) * 16);
+        dma_off[i] = (uint32_t)dma_row[i] * (uint32_t)tok_bytes + dma_col[i];
     }
     auto dma = [&](const char *src, char (*ring)[kTileBytes], int t) {
         char *dst = ring[t & (kRing - 1)];
+        if (t * kKTile + kKTile <= N) {
+            const char *base = src + (size_t)t * kKTile * tok_bytes;
 #pragma unroll
-        for (int i = 0; i < kDmaPerTile; ++i) {
-            const int key = min(t * kKTile + dma_row[i], N - 1);
-            const char *p = src + (size_t)key * tok_bytes + dma_col[i];
-            dma16(p, (uint32_t)(uintptr_t)(dst + (kDmaPerTile * wave + i) * 1024));
+            for (int i = 0; i < kDmaPerTile; ++i)
+                dma16_at(base, dma_off[i], (uint32_t)(uintptr_t)(dst + (kDmaPerTile * wave + i) * 1024));
+        } else {
+#pragma unroll
+            for (int i = 0; i < kDmaPerTile; ++i) {
+                const int key = min(t * kKTile + dma_row[i], N - 1);
+                const char *p = src + (size_t)key * tok_bytes + dma_col[i];
+                dma16(p, (uint32_t)(uintptr_t)(dst + (kDmaPerTile * wave + i) * 1024));
+            }
         }
     };
 
