@@ -99,23 +99,23 @@ struct Mma<_Float16> {
 };
 
 // One 16-byte global load per lane written straight to LDS: lane l's bytes go
-// to LDS address lds + 16 * l (lds wave-uniform, passed in m0). Written as
-// inline assembly so that the compiler, which would otherwise wait for every
-// such load before any later LDS read, leaves the waits to wait_vm below; the
-// instruction has no register result. m0 is set one instruction ahead of its
-// use, as the LDS-load form requires.
+// to LDS address lds + 16 * l (lds wave-uniform, in m0, which the compiler
+// sets as the asm's input). Written as inline assembly so that the compiler,
+// which would otherwise wait for every such load before any later LDS read,
+// leaves the waits to wait_vm below; the instruction has no register result.
+// The s_nop keeps the one wait state the LDS-load form needs after m0 is set.
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
+                 : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
 }
 // The same load from a wave-uniform base (in SGPRs) plus a 32-bit lane offset.
 __device__ __forceinline__ void dma16_at(const void *sbase, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(off), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
+                 : "v"(off), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
 }
 
 // s_waitcnt on the vector-memory counter alone (expcnt and lgkmcnt left free):
