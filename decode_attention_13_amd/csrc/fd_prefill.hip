@@ -412,11 +412,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             rescale = softmax(sc1, p_next);
             // Interleave the block for the scheduler: one MFMA, then three VALU
             // instructions, for each MFMA of the block (left alone, the compiler
-            // bunched the softmax).
+            // bunched the softmax); bf16, whose P.V issues two MFMAs per V
+            // fragment, also takes one LDS read per group (1.5% on the bf16
+            // workload, 3% slower for f16).
             constexpr int kBlockMfma = QB * (8 + 8 * (M::kSplitP ? 2 : 1));
 #pragma unroll
             for (int sg = 0; sg < kBlockMfma; ++sg) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                if constexpr (M::kSplitP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
             }
             sc1 = sc2;
