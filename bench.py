@@ -370,10 +370,14 @@ def bench_prefill(args) -> dict:
     lib = fd.lib()
     code = fd.binding.FD_DTYPE[q.dtype]
     stream = torch.cuda.current_stream()
+    # bf16: the workspace of the f16-V path (the f16 copy of V and its flags), allocated once
+    ws_bytes = fd.prefill_workspace_size(w.B, w.N, w.Hkv, q.dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_ptr = ws.data_ptr() if ws_bytes else None
 
     def step(opt=None):
         rc = lib.fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.N, w.H, w.Hkv, 128, code,
-                            d["scale"], int(w.causal), ctypes.byref(opt) if opt is not None else None,
+                            d["scale"], int(w.causal), ws_ptr, ws_bytes, ctypes.byref(opt) if opt is not None else None,
                             stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"{lib.fd_status_string(rc).decode()}: {lib.fd_last_error().decode()}")
@@ -415,7 +419,8 @@ def bench_prefill(args) -> dict:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "Hkv": w.Hkv, "D": 128, "causal": w.causal,
-                   "flops": flops, "parallelism": "single GPU"},
+                   "flops": flops, "parallelism": "single GPU",
+                   "pv": ("f16 MFMAs on an f16 copy of V (workspace)" if ws_bytes else "f16 MFMAs")},
         "roofline": {"bound": "mfma", "achieved": round(flops / k_mean / 1e12, 2), "peak": PEAK_TFLOPS_16BIT,
                      "unit": "TFLOP/s", "frac": round(flops / k_mean / 1e12 / PEAK_TFLOPS_16BIT, 4),
                      "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),

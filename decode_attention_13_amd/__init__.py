@@ -21,5 +21,7 @@ from .binding import (  # noqa: F401
     options,
     paged_plan,
     paged_workspace_size,
+    prefill_flags,
+    prefill_workspace_size,
     workspace_views,
 )

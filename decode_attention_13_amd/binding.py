@@ -96,7 +96,10 @@ SIGNATURES = {
                                              ctypes.POINTER(FdOptions), ctypes.c_void_p]),
     "fd_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                                  ctypes.c_int, ctypes.POINTER(FdOptions), ctypes.c_void_p]),
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(FdOptions),
+                                  ctypes.c_void_p]),
+    "fd_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     ctypes.c_int]),
     "fd_decode_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, ctypes.POINTER(FdOptions),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
@@ -374,11 +377,26 @@ def fd_paged_decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     return o
 
 
+def prefill_workspace_size(B: int, N: int, Hkv: int, dtype) -> int:
+    """Bytes fd_prefill's workspace needs (bf16: the f16 copy of V and the flag rows; 0 for f16)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().fd_prefill_workspace_size(B, N, Hkv, HEAD_DIM, code))
+
+
+def prefill_flags(ws: torch.Tensor, B: int, N: int, Hkv: int) -> torch.Tensor:
+    """[B, 1024] uint8 view of a bf16 prefill workspace's flag rows (1: that chunk of the
+    sequence's V held a finite value of 65536 or more, so the sequence took the split-P path)."""
+    off = B * N * Hkv * HEAD_DIM * 2
+    return ws[off: off + B * 1024].view(B, 1024)
+
+
 def fd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
                scale: float | None = None, causal: bool = True, opt: FdOptions | None = None,
-               stream=None) -> torch.Tensor:
+               stream=None, ws: torch.Tensor | bool | None = None) -> torch.Tensor:
     """Prefill attention: q [B, N, H, D], k/v [B, N, Hkv, D] (f16/bf16) -> o [B, N, H, D];
-    causal: query i sees keys 0..i."""
+    causal: query i sees keys 0..i. bf16: ws None allocates the workspace of the f16-V
+    path (uninitialised; the library writes it before reading), a tensor is used as the
+    workspace, False passes none (the split-P path)."""
     B, N, H, D = q.shape
     if k.dim() != 4 or k.shape[0] != B or k.shape[1] != N or k.shape[3] != D or v.shape != k.shape:
         raise ValueError("k and v must both be [B, N, Hkv, D] with q's B, N and D")
@@ -391,8 +409,17 @@ def fd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
         raise ValueError("o must have q's shape")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    _check(lib().fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, N, H, k.shape[2], D,
-                            _dtype_code(q.dtype), float(scale), 1 if causal else 0, _opt_ptr(opt),
+    Hkv = k.shape[2]
+    wp, wb = None, 0
+    if ws is not False:
+        need = prefill_workspace_size(B, N, Hkv, q.dtype)
+        if need and ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if isinstance(ws, torch.Tensor):
+            _require(ws, "ws", torch.uint8)
+            wp, wb = ws.data_ptr(), ws.numel()
+    _check(lib().fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, N, H, Hkv, D,
+                            _dtype_code(q.dtype), float(scale), 1 if causal else 0, wp, wb, _opt_ptr(opt),
                             _stream_handle(stream)))
     return o
 

@@ -669,8 +669,15 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
                       D, num_pages, max_blocks, max_seq_len, total_kv, dtype, ws, ws_bytes, opt, stream);
 }
 
+size_t fd_prefill_workspace_size(int B, int N, int Hkv, int D, fd_dtype dtype) {
+    if (dtype != FD_DTYPE_BF16 || B <= 0 || N <= 0 || Hkv <= 0 || D != 128) return 0;
+    if ((long long)B * Hkv * ((N + 63) / 64) > INT_MAX) return 0;  // fd_prefill refuses these sizes
+    return fd::prefill_workspace_bytes(B, N, Hkv);
+}
+
 fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B, int N, int H, int Hkv, int D,
-                     fd_dtype dtype, float scale, int causal, const fd_options *opt, void *stream) {
+                     fd_dtype dtype, float scale, int causal, void *ws, size_t ws_bytes, const fd_options *opt,
+                     void *stream) {
     fd_status s = check_common(B, H, Hkv, D, dtype, opt);
     if (s != FD_OK) return s;
     if (dtype != FD_DTYPE_F16 && dtype != FD_DTYPE_BF16)
@@ -685,6 +692,14 @@ fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B
     if (!q || !k || !v || !o) return fail(FD_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(FD_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    // The workspace serves bf16 only (the f16 copy of V); f16 ignores it.
+    if (dtype != FD_DTYPE_BF16) ws = nullptr;
+    if (ws) {
+        const size_t need = fd::prefill_workspace_bytes(B, N, Hkv);
+        if (ws_bytes < need)
+            return fail(FD_ERR_WORKSPACE, "prefill workspace is %zu bytes, %zu needed", ws_bytes, need);
+        if (!aligned16(ws)) return fail(FD_ERR_INVALID_ARG, "the prefill workspace must be 16-byte aligned");
+    }
     fd::PrefillArgs a{};
     a.q = q;
     a.k = k;
@@ -703,7 +718,7 @@ fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B
     if (a.scale_log2 == 0.f) a.scale_log2 = FLT_MIN;
     hipEvent_t ev0 = opt ? reinterpret_cast<hipEvent_t>(opt->split_begin_event) : nullptr;
     hipEvent_t ev1 = opt ? reinterpret_cast<hipEvent_t>(opt->split_end_event) : nullptr;
-    const hipError_t e = fd::launch_prefill(dtype, a, reinterpret_cast<hipStream_t>(stream), ev0, ev1);
+    const hipError_t e = fd::launch_prefill(dtype, a, ws, reinterpret_cast<hipStream_t>(stream), ev0, ev1);
     if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "prefill kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
 }

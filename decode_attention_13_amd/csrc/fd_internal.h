@@ -118,14 +118,38 @@ inline hipError_t launch_timed(const void *fn, const LaunchShape &s, void **args
 hipError_t launch_merge(fd_dtype dtype, bool paged, int B, const MergeArgs &a, hipStream_t stream);
 
 // Prefill: q, o [B, N, H, D]; k, v [B, N, Hkv, D].
+// bf16 prefill with a workspace: V is first converted to an f16 copy (exact for
+// |v| < 65536), with one flag byte per chunk of a sequence's V rows saying
+// whether some value did not fit. Each sequence owns a row of kPrefillFlagRow
+// flag bytes, of which the first flag_chunks are written.
+constexpr int kPrefillFlagRow = 1024;
+constexpr int kPrefillConvMinRows = 128;  // 256-byte V rows per conversion workgroup, at least
+enum PrefillFlagMode : int {
+    kPrefillNoFlags = 0,       // run every sequence
+    kPrefillRunIfClean = 1,    // the f16-V kernel: skip sequences whose V did not convert
+    kPrefillRunIfFlagged = 2,  // the split-P kernel after it: run only those sequences
+};
+
 struct PrefillArgs {
-    const void *q, *k, *v;
+    const void *q, *k, *v;  // v: the caller's V, or its f16 copy (kPrefillRunIfClean)
     void *o;
     int B, N, H, Hkv, G;    // G = H / Hkv
     int causal;             // 1: query i sees keys 0 .. i
     int q_tiles;            // query tiles (set by the launcher)
     float scale_log2;       // scale * log2(e)
+    const uint8_t *flags;   // B rows of kPrefillFlagRow bytes (flag modes 1 and 2)
+    int flag_chunks;        // flags written per row
+    int flag_mode;          // PrefillFlagMode
 };
-hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+// Workspace bytes of the bf16 f16-V path: the f16 copy of V, then the flag rows.
+size_t prefill_workspace_bytes(int B, int N, int Hkv);
+
+// f16 and bf16 without a workspace: one kernel. bf16 with a workspace (at
+// least prefill_workspace_bytes): conversion, the f16-V kernel, and the
+// split-P kernel for the sequences that did not convert. start / stop (may be
+// null) bracket the kernel that does the attention of the clean sequences.
+hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, void *ws, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop);
 
 }  // namespace fd

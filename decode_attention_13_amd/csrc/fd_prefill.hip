@@ -31,6 +31,13 @@
 // the latency of L2 and HBM without holding the loop. A tile is 32 unpadded
 // 256-byte rows with their 16-byte chunks permuted per row (swz below), so the
 // K fragment reads and the transposed V reads both spread over all banks.
+//
+// bf16 with a workspace takes three launches: prefill_convert_v_kernel writes
+// an f16 copy of V (exact below 65536 in magnitude) and a flag per chunk of
+// each sequence's V rows; prefill_kernel<bf16, f16> runs P.V on f16 MFMAs from
+// that copy, P in f16, for the sequences with no flag set; and
+// prefill_kernel<bf16, bf16> reruns the flagged ones with the split P. Without
+// a workspace the last kernel runs alone, on every sequence.
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -135,10 +142,27 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xf << 8) | (0x7 << 4) | (N & 0xf));
 }
 
-// Two waves per SIMD (two workgroups per CU): the register budget is 256.
-template <typename T>
+// Whether sequence b's V holds a value outside f16's range: the 1 KiB flag row
+// of the sequence, 16 bytes a lane, entries at or past `chunks` masked off.
+__device__ __forceinline__ bool v_flagged(uint4 fl, int chunks, int lane) {
+    const uint32_t w[4] = {fl.x, fl.y, fl.z, fl.w};
+    uint32_t any = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int cnt = min(max(chunks - (16 * lane + 4 * j), 0), 4);  // valid flag bytes in word j
+        any |= w[j] & (cnt >= 4 ? 0xffffffffu : (1u << (8 * cnt)) - 1u);
+    }
+    return __builtin_amdgcn_ballot_w64(any != 0) != 0;
+}
+
+// TQ: type of q, k and o (the S MFMAs); TV: type of v and of P (the P.V
+// MFMAs). <bf16, f16> runs on the f16 copy of V that the conversion kernel
+// below writes. Two waves per SIMD (two workgroups per CU): the register
+// budget is 256.
+template <typename TQ, typename TV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
-    using M = Mma<T>;
+    using MS = Mma<TQ>;
+    using M = Mma<TV>;
     constexpr int kQTile = kWaves * kWaveQ;  // queries per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: wave-level branches stay scalar
@@ -167,6 +191,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int b = unit / a.H;
     const int kvh = h / a.G;
     const int N = a.N;
+    // The split-P kernel behind the f16 one runs only the sequences whose V
+    // did not convert: the others leave before any tile load.
+    if (a.flag_mode == kPrefillRunIfFlagged &&
+        !v_flagged(load16(a.flags + (size_t)b * kPrefillFlagRow + 16 * lane), a.flag_chunks, lane))
+        return;
     const int q0 = qt * kQTile + wave * kWaveQ;  // this wave's first query
     const int q_last = q0 + kWaveQ - 1;
     const int kv_end = a.causal ? min(N, (qt + 1) * kQTile) : N;
@@ -184,9 +213,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // wave + i) .. + 3, lane l the 16 bytes at l * 16 (row + l / 16, stored
     // chunk l % 16), which hold chunk (l % 16) ^ swz(row) of that key's row.
     // Keys past N re-read key N - 1 (never used: masked, or past the workgroup).
-    const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * sizeof(T);
-    const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
-    const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * sizeof(T);
+    static_assert(sizeof(TQ) == 2 && sizeof(TV) == 2, "K and V rows are 256 bytes");
+    const size_t tok_bytes = (size_t)a.Hkv * kHeadDim * 2;
+    const char *kg = reinterpret_cast<const char *>(a.k) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * 2;
+    const char *vg = reinterpret_cast<const char *>(a.v) + ((size_t)b * N * a.Hkv + kvh) * kHeadDim * 2;
     // Lane offsets within a tile (row * token bytes + chunk; 32 rows of at most
     // 65535 * 256 bytes fit in 32 bits): a tile wholly below N is one scalar base
     // plus these, with no per-lane address arithmetic; a tile reaching past N
@@ -241,7 +271,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const u32x4 kr = *(lds_u32x4 *)(kt + (((2 * ks + hb) ^ sw) << 4));
-            r.v = M::mma32(make_uint4(kr.x, kr.y, kr.z, kr.w), qf[ks], r.v);
+            r.v = MS::mma32(make_uint4(kr.x, kr.y, kr.z, kr.w), qf[ks], r.v);
         }
         return r;
     };
@@ -358,6 +388,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // query rows, one wait for all of them (so the waits the compiler places for
     // the queries count every load in flight), then V1 K3 V2; K4 shares its ring
     // slot with K0 and follows the barrier after K0 is read.
+    // On the f16 copy of V, the sequence's flag row comes first, so the one wait
+    // covers it too.
+    uint4 vflags = make_uint4(0u, 0u, 0u, 0u);
+    if (a.flag_mode == kPrefillRunIfClean) vflags = load16(a.flags + (size_t)b * kPrefillFlagRow + 16 * lane);
     dma(kg, sK, 0);
     dma(kg, sK, 1);
     dma(vg, sV, 0);
@@ -365,7 +399,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Q fragments (B operand of S): query q0 + qc, head-dim slots 16 ks + 8 hb .. + 8.
     {
         const int qr = min(q0 + qc, N - 1);
-        const T *qrow = reinterpret_cast<const T *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
+        const TQ *qrow = reinterpret_cast<const TQ *>(a.q) + (((size_t)b * N + qr) * a.H + h) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = load16(qrow + ks * 16 + hb * 8);
     }
@@ -382,6 +416,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     wait_vm<0>();
+    // A sequence whose V did not convert is left to the split-P kernel (every
+    // wave reads the same row and leaves; no load is in flight).
+    if (a.flag_mode == kPrefillRunIfClean && v_flagged(vflags, a.flag_chunks, lane)) return;
     dma(vg, sV, 1);
     dma(kg, sK, 3);
     dma(vg, sV, 2);
@@ -436,36 +473,120 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int q_me = q0 + qc;
         if (q_me < N) {
             const float inv = 1.f / ls;
-            T *orow = reinterpret_cast<T *>(a.o) + (((size_t)b * N + q_me) * a.H + h) * kHeadDim;
+            TQ *orow = reinterpret_cast<TQ *>(a.o) + (((size_t)b * N + q_me) * a.H + h) * kHeadDim;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
-                    typedef typename Pair<T>::type P2;
+                    typedef typename Pair<TQ>::type P2;
                     P2 *dst = reinterpret_cast<P2 *>(orow + db * 32 + 8 * i4 + 4 * hb);
-                    dst[0] = Pair<T>::make(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv);
-                    dst[1] = Pair<T>::make(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+                    dst[0] = Pair<TQ>::make(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv);
+                    dst[1] = Pair<TQ>::make(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
                 }
         }
     }
 }
 
+// The f16 copy of a bf16 V for the f16-V prefill: one workgroup per chunk of
+// rows (256-byte rows of one token and KV head) of one sequence. A bf16 value
+// converts exactly when |v| < 65536 (bf16 has 8 significant bits, f16 11 and
+// its exponent range; below 2^-14 f16 rounds to a multiple of 2^-24, an error
+// under 2^-25). The chunk's flag byte records whether some finite value was
+// 65536 or more; infinities and NaNs convert to themselves. Every flag of the
+// row up to flag_chunks is written on each call, so no clearing is needed.
+struct ConvertArgs {
+    const void *v;   // [B, N, Hkv, 128] bf16
+    void *v16;       // the same layout, f16
+    uint8_t *flags;  // [B, kPrefillFlagRow]
+    long long rows;  // N * Hkv, rows per sequence
+    int rows_per_chunk, chunks;
+};
+
+constexpr int kConvThreads = 256;
+constexpr int kConvUnroll = 8;  // 16-byte loads in flight per lane
+
+__global__ __launch_bounds__(kConvThreads) void prefill_convert_v_kernel(ConvertArgs c) {
+    const int b = blockIdx.x / c.chunks;
+    const int ch = blockIdx.x - b * c.chunks;
+    const long long row0 = (long long)ch * c.rows_per_chunk;
+    const long long nrows = min((long long)c.rows_per_chunk, c.rows - row0);
+    const long long pieces = nrows * (kHeadDim * 2 / 16);  // 16-byte pieces of the chunk
+    const size_t first = ((size_t)b * c.rows + row0) * (kHeadDim * 2);  // byte offset of the chunk
+    const char *src = reinterpret_cast<const char *>(c.v) + first;
+    char *dst = reinterpret_cast<char *>(c.v16) + first;
+    bool bad = false;
+    for (long long p0 = 0; p0 < pieces; p0 += kConvThreads * kConvUnroll) {
+        uint4 x[kConvUnroll];
+#pragma unroll
+        for (int i = 0; i < kConvUnroll; ++i) {
+            const long long p = p0 + i * kConvThreads + (int)threadIdx.x;
+            if (p < pieces) x[i] = load_stream16(src + (size_t)p * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < kConvUnroll; ++i) {
+            const long long p = p0 + i * kConvThreads + (int)threadIdx.x;
+            if (p >= pieces) continue;
+            const uint32_t w[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = __builtin_bit_cast(float, w[j] << 16);
+                const float hi = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+                o[j] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
+                const float alo = fabsf(lo), ahi = fabsf(hi);  // NaN compares false, inf is not <= max
+                bad |= (alo >= 65536.f && alo <= __FLT_MAX__) || (ahi >= 65536.f && ahi <= __FLT_MAX__);
+            }
+            *reinterpret_cast<uint4 *>(dst + (size_t)p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) c.flags[(size_t)b * kPrefillFlagRow + ch] = bad ? 1 : 0;
+}
+
 }  // namespace
 
-hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+size_t prefill_workspace_bytes(int B, int N, int Hkv) {
+    return (size_t)B * N * Hkv * kHeadDim * 2 + (size_t)B * kPrefillFlagRow;
+}
+
+hipError_t launch_prefill(fd_dtype dtype, const PrefillArgs &a, void *ws, hipStream_t st, hipEvent_t e0,
+                          hipEvent_t e1) {
     PrefillArgs arg = a;
     arg.q_tiles = (a.N + kWaves * kWaveQ - 1) / (kWaves * kWaveQ);
+    arg.flags = nullptr;
+    arg.flag_chunks = 0;
+    arg.flag_mode = kPrefillNoFlags;
     LaunchShape s{dim3(arg.q_tiles * a.H * a.B), dim3(kThreads)};
     void *args[] = {&arg};
-    switch (dtype) {
-        case FD_DTYPE_F16:
-            return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<_Float16>), s, args, st,
-                                e0, e1);
-        case FD_DTYPE_BF16:
-            return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16>), s, args, st,
-                                e0, e1);
-        default: return hipErrorInvalidValue;
-    }
+    if (dtype == FD_DTYPE_F16)
+        return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<_Float16, _Float16>), s, args, st, e0, e1);
+    if (dtype != FD_DTYPE_BF16) return hipErrorInvalidValue;
+    if (!ws)
+        return launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16, __bf16>), s, args, st, e0, e1);
+    // At most kPrefillFlagRow chunks per sequence, of at least
+    // kPrefillConvMinRows rows each.
+    ConvertArgs c{};
+    c.v = a.v;
+    c.v16 = ws;
+    c.rows = (long long)a.N * a.Hkv;
+    const long long per = (c.rows + kPrefillFlagRow - 1) / kPrefillFlagRow;
+    c.rows_per_chunk = (int)(per > kPrefillConvMinRows ? per : kPrefillConvMinRows);
+    c.chunks = (int)((c.rows + c.rows_per_chunk - 1) / c.rows_per_chunk);
+    c.flags = reinterpret_cast<uint8_t *>(ws) + (size_t)a.B * a.N * a.Hkv * kHeadDim * 2;
+    void *cargs[] = {&c};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_convert_v_kernel),
+                                   dim3((unsigned)a.B * c.chunks), dim3(kConvThreads), cargs, 0, st);
+    if (e != hipSuccess) return e;
+    arg.v = ws;
+    arg.flags = c.flags;
+    arg.flag_chunks = c.chunks;
+    arg.flag_mode = kPrefillRunIfClean;
+    e = launch_timed(reinterpret_cast<const void *>(&prefill_kernel<__bf16, _Float16>), s, args, st, e0, e1);
+    if (e != hipSuccess) return e;
+    arg.v = a.v;
+    arg.flag_mode = kPrefillRunIfFlagged;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel<__bf16, __bf16>), s.grid, s.block, args, 0,
+                           st);
 }
 
 }  // namespace fd

@@ -345,12 +345,32 @@ fd_status fd_paged_decode_fp8kv(const void *q, const void *k_cache, const void *
  *   N      0 .. 2^30 (N = 0 launches nothing); B, H <= 65535 and
  *          B * H * ceil(N / 64) < 2^31 (else FD_ERR_UNSUPPORTED)
  *   scale  any finite value (a negative one flips the sign of every score)
+ *   ws, ws_bytes  bf16 only (f16 ignores them), device memory that must not
+ *          overlap q, k, v or o. NULL: P.V runs on bf16 MFMAs with P split
+ *          into two bf16 parts (two MFMAs per step). Otherwise at least
+ *          fd_prefill_workspace_size() bytes (else FD_ERR_WORKSPACE), 16-byte
+ *          aligned: a first kernel writes an f16 copy of V there (exact for
+ *          |v| < 65536) and a flag per chunk of each sequence's V, the
+ *          attention then runs P.V on f16 MFMAs with P in f16 (one MFMA per
+ *          step), and a last kernel reruns, with the split P, the sequences
+ *          whose V held a finite value of 65536 or more. Results agree
+ *          within the same tolerance either way.
  *   opt    may be NULL; only split_begin_event / split_end_event are used, and
- *          they time the prefill kernel
- * No workspace. Asynchronous on `stream`; errors as for fd_decode.
+ *          they time the kernel that runs the attention of the sequences
+ *          (with a workspace: the f16-V kernel alone)
+ * Asynchronous on `stream`; errors as for fd_decode. The workspace is
+ * read and written on `stream`: calls that share one may not overlap.
  */
 fd_status fd_prefill(const void *q, const void *k, const void *v, void *o, int B, int N, int H, int Hkv, int D,
-                     fd_dtype dtype, float scale, int causal, const fd_options *opt, void *stream);
+                     fd_dtype dtype, float scale, int causal, void *ws, size_t ws_bytes, const fd_options *opt,
+                     void *stream);
+
+/*
+ * Workspace bytes fd_prefill uses for a bf16 prefill of these sizes: the f16
+ * copy of V (B * N * Hkv * D * 2 bytes) and 1024 flag bytes per sequence.
+ * 0 for f16, for arguments fd_prefill would refuse, and for N = 0.
+ */
+size_t fd_prefill_workspace_size(int B, int N, int Hkv, int D, fd_dtype dtype);
 
 /* Static name of a status code. */
 const char *fd_status_string(fd_status s);

@@ -256,8 +256,9 @@ def test_no_device_is_reported():
 def test_prefill_rejects_bad_arguments_without_a_device():
     lib = fd.lib()
 
-    def call(q=16, k=16, v=16, o=16, B=1, N=64, H=8, Hkv=2, D=128, dtype=2, scale=0.1, causal=1, opt=None):
-        return lib.fd_prefill(q, k, v, o, B, N, H, Hkv, D, dtype, scale, causal, opt, None)
+    def call(q=16, k=16, v=16, o=16, B=1, N=64, H=8, Hkv=2, D=128, dtype=2, scale=0.1, causal=1, opt=None,
+             ws=None, ws_bytes=0):
+        return lib.fd_prefill(q, k, v, o, B, N, H, Hkv, D, dtype, scale, causal, ws, ws_bytes, opt, None)
 
     assert "fd_prefill" in declared_functions()
     assert call(N=0, q=None) == 0  # nothing to do: no launch, no pointer use
@@ -275,6 +276,16 @@ def test_prefill_rejects_bad_arguments_without_a_device():
     assert call(B=65535, H=65535, Hkv=65535, N=64) == 2  # grid beyond 31 bits
     assert lib.fd_status_string(call(opt=ctypes.byref(fd.options(force_chunk=100)))).decode() == "FD_ERR_INVALID_ARG"
     assert call(scale=float("nan")) == 1 and "scale" in lib.fd_last_error().decode()
+    # bf16 with a workspace: the f16 copy of V plus a 1 KiB flag row per sequence
+    need = lib.fd_prefill_workspace_size(3, 64, 2, 128, 2)
+    assert need == 3 * 64 * 2 * 128 * 2 + 3 * 1024
+    assert lib.fd_prefill_workspace_size(3, 64, 2, 128, 1) == 0  # f16 needs none
+    assert lib.fd_prefill_workspace_size(3, 0, 2, 128, 2) == 0
+    assert lib.fd_prefill_workspace_size(3, 64, 2, 64, 2) == 0
+    assert lib.fd_prefill_workspace_size(65535, 1 << 30, 65535, 128, 2) == 0  # sizes fd_prefill refuses
+    assert call(B=3, dtype=2, ws=256, ws_bytes=need - 1) == 3  # FD_ERR_WORKSPACE, before any launch
+    assert "workspace" in lib.fd_last_error().decode()
+    assert call(B=3, dtype=2, ws=8, ws_bytes=need) == 1  # misaligned workspace
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

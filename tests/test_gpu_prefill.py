@@ -1,6 +1,10 @@
 """GPU parity of fd_prefill (many-query attention, optional causal mask) against
 the float64 oracle, through the C ABI. Tolerance as for the decode path with
-16-bit inputs: |gpu - ref| <= 2e-3 + 1e-2 |ref| against the unrounded oracle."""
+16-bit inputs: |gpu - ref| <= 2e-3 + 1e-2 |ref| against the unrounded oracle.
+
+bf16 calls go through the binding's default, the workspace path (V converted to
+f16, P.V on f16 MFMAs, sequences whose V does not convert rerun with the split
+P); the tests marked "split" pass no workspace and run the split-P kernel alone."""
 import sys
 
 import numpy as np
@@ -30,8 +34,8 @@ def device():
     torch.cuda.synchronize()
 
 
-def run(d, dev, causal):
-    o = fd.fd_prefill(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), scale=d["scale"], causal=causal)
+def run(d, dev, causal, ws=None):
+    o = fd.fd_prefill(d["q"].to(dev), d["k"].to(dev), d["v"].to(dev), scale=d["scale"], causal=causal, ws=ws)
     torch.cuda.synchronize()
     return o.cpu()
 
@@ -80,11 +84,13 @@ def test_first_row_is_exact(dtype, device):
     assert torch.equal(o[:, 0], want)
 
 
+@pytest.mark.parametrize("path", ["workspace", "split"])
 @pytest.mark.parametrize("causal", [True, False])
-def test_bf16_tiles_beyond_f16(causal, device):
+def test_bf16_tiles_beyond_f16(causal, path, device):
     """bf16 V far outside f16's range (|v| from 65280 up to 1e30) in key rows of
     several tiles, loaded by different waves: P.V on bf16 MFMAs with P split in
-    a truncated hi and a rounded lo part keeps them exact to 16 bits of P.
+    a truncated hi and a rounded lo part keeps them exact to 16 bits of P. With
+    the workspace both sequences are flagged and take that kernel too.
 
     Outputs here can be small sums of terms near 1e4 that cancel, so the bound
     also carries the conditioning of each output: P is kept to a relative 2^-15
@@ -98,8 +104,14 @@ def test_bf16_tiles_beyond_f16(causal, device):
     v[1, 192 + 4, 0, 77] = -65536.0
     d["v"] = v.to(torch.bfloat16)
     assert d["v"][0, 96 + 12, 1, 5].item() == 65280.0
-    announce(f"bf16 tiles beyond f16, causal={causal}")
-    o = run(d, device, causal)
+    announce(f"bf16 tiles beyond f16, causal={causal}, {path}")
+    ws = None
+    if path == "workspace":
+        ws = torch.empty(fd.prefill_workspace_size(2, 200, 2, torch.bfloat16), dtype=torch.uint8, device=device)
+    o = run(d, device, causal, ws if path == "workspace" else False)
+    if path == "workspace":
+        flags = fd.prefill_flags(ws, 2, 200, 2).cpu()
+        assert flags[:, :4].amax(dim=1).tolist() == [1, 1]  # 400 rows: 4 chunks of 128 per sequence
     ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
     cond, _ = oracle.prefill_attention(d["q"], d["k"], d["v"].abs(), d["scale"], causal)
     err = np.abs(o.to(torch.float64).numpy() - ref)
@@ -197,3 +209,74 @@ def test_head_groupings(B, N, H, Hkv, device):
         o = run(d, device, causal)
         ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
         assert_close(o, ref, f"B={B} N={N} H={H}/{Hkv} causal={causal}")
+
+
+def _chunks(N, Hkv):
+    rows = N * Hkv
+    per = max(128, -(-rows // 1024))
+    return -(-rows // per)
+
+
+def test_bf16_workspace_flags_per_sequence(device):
+    """Three sequences, one V value of 70000 in sequence 1 (no f16 for it) and
+    65280, the largest bf16 value below 65536, in sequence 2 (exact in f16):
+    only sequence 1 is flagged and rerun with the split P; all three match the
+    oracle. The same workspace then serves a batch with no such value, and no
+    flag of the first call survives."""
+    B, N, H, Hkv = 3, 300, 8, 2
+    d = inputs.prefill_inputs(B, N, H, Hkv, 128, "bf16", 570)
+    v = d["v"].clone()
+    v[1, 217, 1, 40] = 70000.0
+    v[2, 5, 0, 3] = -65280.0
+    assert v[1, 217, 1, 40].item() == 70144.0 and v[2, 5, 0, 3].item() == -65280.0  # bf16 rounding
+    d["v"] = v
+    ws = torch.empty(fd.prefill_workspace_size(B, N, Hkv, torch.bfloat16), dtype=torch.uint8, device=device)
+    c = _chunks(N, Hkv)
+    for causal in (True, False):
+        announce(f"flags per sequence causal={causal}")
+        o = run(d, device, causal, ws)
+        flags = fd.prefill_flags(ws, B, N, Hkv)[:, :c].cpu()
+        assert flags.amax(dim=1).tolist() == [0, 1, 0]
+        assert flags[1].tolist() == [1 if i == (217 * Hkv + 1) // 128 else 0 for i in range(c)]
+        ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
+        assert_close(o, ref, f"flags per sequence causal={causal}")
+    d2 = inputs.prefill_inputs(B, N, H, Hkv, 128, "bf16", 571)
+    announce("flags cleared by the next call")
+    o = run(d2, device, True, ws)
+    assert int(fd.prefill_flags(ws, B, N, Hkv)[:, :c].max()) == 0
+    ref, _ = oracle.prefill_attention(d2["q"], d2["k"], d2["v"], d2["scale"], True)
+    assert_close(o, ref, "second call")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 33, 1000])
+def test_bf16_split_path(N, causal, device):
+    """bf16 without a workspace: the split-P kernel alone, GQA 8/2, two sequences."""
+    d = inputs.prefill_inputs(2, N, 8, 2, 128, "bf16", 580 + N)
+    announce(f"split path N={N} causal={causal}")
+    o = run(d, device, causal, False)
+    ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], d["scale"], causal)
+    assert_close(o, ref, f"split N={N} causal={causal}")
+
+
+def test_bf16_large_batch_many_chunks(device):
+    """A sequence whose V rows exceed 1024 * 128 (N = 8192, Hkv = 32): chunks of
+    more than 128 rows, the flag row full; one value of 1e5 near the end of the
+    second sequence flags it alone. Sampled rows against the oracle's decode."""
+    B, N, H, Hkv = 2, 8192, 32, 32
+    d = inputs.prefill_inputs(B, N, H, Hkv, 128, "bf16", 590)
+    v = d["v"].clone()
+    v[1, N - 3, 30, 100] = 1e5
+    d["v"] = v
+    c = _chunks(N, Hkv)
+    assert c == 1024
+    ws = torch.empty(fd.prefill_workspace_size(B, N, Hkv, torch.bfloat16), dtype=torch.uint8, device=device)
+    announce("large batch, full flag rows")
+    o = run(d, device, True, ws)
+    flags = fd.prefill_flags(ws, B, N, Hkv).cpu()
+    assert flags[0].max().item() == 0 and flags[1].tolist() == [1 if i == c - 1 else 0 for i in range(c)]
+    for b, i, h in [(0, 0, 0), (0, N - 1, 31), (1, 4000, 17), (1, N - 1, 30), (1, N - 2, 31)]:
+        g = h // (H // Hkv)
+        ref, _ = oracle.decode_attention(d["q"][b, i, h:h + 1], d["k"][b, :i + 1, g:g + 1], d["v"][b, :i + 1, g:g + 1],
+                                         d["scale"])
+        assert_close(o[b, i, h:h + 1], ref, f"large batch b={b} row {i} head {h}")
