@@ -112,6 +112,10 @@ struct Mma<_Float16> {
         hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
         lo = 0;
     }
+    // acc + the two f16 values of a packed pair
+    __device__ static float sum2(uint32_t pair, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+    }
 };
 
 // One 16-byte global load per lane written straight to LDS: lane l's bytes go
@@ -319,9 +323,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             pe[i] = exp2_fast(__builtin_fmaf(sc.v[i], sl, -mu));
-            ps += pe[i];
+            if constexpr (M::kSplitP) ps += pe[i];
         }
-        lsum = __builtin_fmaf(lsum, alpha, ps);
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
             uint32_t hw[4], lw[4];
@@ -329,7 +332,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int e2 = 0; e2 < 4; ++e2) M::split2(pe[8 * kv + 2 * e2], pe[8 * kv + 2 * e2 + 1], hw[e2], lw[e2]);
             pr.hi[kv] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             if constexpr (M::kSplitP) pr.lo[kv] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            // f16 P: the sum is taken over the rounded values P.V uses, two per
+            // v_dot2_f32_f16.
+            if constexpr (!M::kSplitP)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) ps = M::sum2(hw[e2], ps);
         }
+        lsum = __builtin_fmaf(lsum, alpha, ps);
         return __builtin_amdgcn_ballot_w64(rescale) != 0;
     };
     auto rescale_acc = [&]() {
