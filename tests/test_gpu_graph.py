@@ -157,3 +157,39 @@ def test_paged_noalloc_step_replays(device):
         assert torch.equal(got, ref), r
         if r == 0:
             assert torch.equal(got, first)
+
+
+def test_bf16_prefill_workspace_replays(device):
+    """The bf16 prefill with a workspace (conversion, attention, split-P rerun:
+    three launches, no memset) captured once and replayed with new q, k and v
+    copied in; the second set holds a value no f16 can carry, so one replay
+    takes the split-P kernel for that sequence. Every replay equals an eager
+    call bit for bit."""
+    B, N, H, Hkv = 2, 300, 8, 2
+    sets = [inputs.prefill_inputs(B, N, H, Hkv, 128, "bf16", 600 + r) for r in range(3)]
+    sets[1]["v"][1, 150, 0, 9] = 1e6
+    dev = [{n: sets[r][n].to(device) for n in ("q", "k", "v")} for r in range(3)]
+    static = {n: dev[0][n].clone() for n in ("q", "k", "v")}
+    o_static = torch.empty_like(static["q"])
+    need = fd.prefill_workspace_size(B, N, Hkv, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_eager = torch.empty(need, dtype=torch.uint8, device=device)
+    scale = sets[0]["scale"]
+    fd.fd_prefill(static["q"], static["k"], static["v"], o=o_static, scale=scale, causal=True, ws=ws)
+    torch.cuda.synchronize()
+    announce("prefill capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fd.fd_prefill(static["q"], static["k"], static["v"], o=o_static, scale=scale, causal=True, ws=ws)
+    for r in range(REPLAYS):
+        announce(f"prefill replay {r}")
+        for n in ("q", "k", "v"):
+            static[n].copy_(dev[r % 3][n])
+        g.replay()
+        torch.cuda.synchronize()
+        got = o_static.clone()
+        ref = fd.fd_prefill(dev[r % 3]["q"], dev[r % 3]["k"], dev[r % 3]["v"], scale=scale, causal=True, ws=ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), r
+        flagged = fd.prefill_flags(ws, B, N, Hkv)[:, :5].amax(dim=1).tolist()
+        assert flagged == ([0, 1] if r % 3 == 1 else [0, 0]), (r, flagged)
