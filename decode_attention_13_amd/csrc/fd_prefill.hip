@@ -264,20 +264,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     struct Scores {
         f32x16 v;  // element i: key 8 (i / 4) + 4 hb + i % 4 of the tile, query q0 + qc
     };
-    // S^T of tile t from the K ring: for k step ks (16 head-dim slots), lane l
-    // reads key row l % 32, chunk 2 ks + hb (stored at that chunk ^ swz(row)).
-    auto scores = [&](int t) {
-        lds_char *kt = (lds_char *)(uintptr_t)sK[t & (kRing - 1)] + qc * kRow;
-        const int sw = swz(qc);
-        Scores r;
+    // The lane's LDS byte offsets within a ring slot, formed once: each
+    // fragment read is then the slot's base plus one of these.
+    // K (S^T, k step ks of 16 head-dim slots): key row l % 32, chunk 2 ks + hb,
+    // stored at that chunk ^ swz(row).
+    uint32_t k_off[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) k_off[ks] = (uint32_t)(qc * kRow + (((2 * ks + hb) ^ swz(qc)) << 4));
+    // V^T for head-dim block db, k step kv, lane l (group G = l / 16, c = l %
+    // 16): transposed 8-byte reads of key rows 16 kv + 4 hb + c / 4 and the same
+    // + 8, columns db*32 + 16 (G % 2) + 4 (c % 4) .. + 3 (chunk 4 db + 2 (G % 2)
+    // + (c % 4) / 2, stored at that chunk ^ swz(row)); lane l receives column
+    // db*32 + l % 32. Rows 16 apart share swz, so k step 1 is k step 0 + 4096.
+    uint32_t v_off[8];  // [2 db + lh]
+    {
+        const int cc = lane & 15, bq = cc & 3;
+        const int r0 = 4 * hb + (cc >> 2);  // row within the 8-row block, 0..7
+        const int cpart = 2 * ((lane >> 4) & 1) + (bq >> 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int lh = 0; lh < 2; ++lh) {
+                const int r = r0 + 8 * lh;
+                v_off[2 * db + lh] = (uint32_t)(r * kRow + (((4 * db + cpart) ^ swz(r)) << 4) + (bq & 1) * 8);
+            }
+    }
+
+    // S^T of tile t from the K ring.
+    auto scores = [&](int t, Scores &r) {
+        lds_char *kt = (lds_char *)(uintptr_t)sK[t & (kRing - 1)];
 #pragma unroll
         for (int i = 0; i < 16; ++i) r.v[i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const u32x4 kr = *(lds_u32x4 *)(kt + (((2 * ks + hb) ^ sw) << 4));
+            const u32x4 kr = *(lds_u32x4 *)(kt + k_off[ks]);
             r.v = MS::mma32(make_uint4(kr.x, kr.y, kr.z, kr.w), qf[ks], r.v);
         }
-        return r;
     };
 
     // Masked scores become -inf, so their P is exactly 0: keys at or past N,
@@ -346,27 +368,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int db = 0; db < 4; ++db) acc[db] *= alpha;
     };
 
-    // O^T += V^T . P^T for tile t from the V ring. V^T for head-dim block db and
-    // k step kv, lane l (group G = l / 16, c = l % 16): transposed 8-byte reads
-    // of key rows 16 kv + 4 hb + c / 4 and the same + 8, columns db*32 +
-    // 16 (G % 2) + 4 (c % 4) .. + 3 (chunk 4 db + 2 (G % 2) + (c % 4) / 2,
-    // stored at that chunk ^ swz(row)); lane l receives column db*32 + l % 32.
+    // O^T += V^T . P^T for tile t from the V ring (reads at v_off above).
     auto pv = [&](int t, const Probs &pr) {
         lds_char *vt = (lds_char *)(uintptr_t)sV[t & (kRing - 1)];
-        const int cc = lane & 15, bq = cc & 3;
-        const int r0 = 4 * hb + (cc >> 2);  // row within the 8-row block, 0..7
-        const int half = (bq & 1) * 8;
-        const int cpart = 2 * ((lane >> 4) & 1) + (bq >> 1);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int kv = 0; kv < 2; ++kv) {
-                const int ra = 16 * kv + r0, rb = ra + 8;
-                const int lc = 4 * db + cpart;
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(vt + ra * kRow + ((lc ^ swz(ra)) << 4) + half));
+                    (lds_i16x4 *)(vt + v_off[2 * db] + kv * 16 * kRow));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(vt + rb * kRow + ((lc ^ swz(rb)) << 4) + half));
+                    (lds_i16x4 *)(vt + v_off[2 * db + 1] + kv * 16 * kRow));
                 const u32x2v lo2 = __builtin_bit_cast(u32x2v, lo);
                 const u32x2v hi2 = __builtin_bit_cast(u32x2v, hi);
                 const uint4 va = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
@@ -432,8 +444,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     dma(kg, sK, 3);
     dma(vg, sV, 2);
     __builtin_amdgcn_s_barrier();
-    Scores sc0 = scores(0);
-    Scores sc1 = scores(1);  // tile 1, or discarded
+    Scores sc0, sc1;
+    scores(0, sc0);
+    scores(1, sc1);  // tile 1, or discarded
     if (masked(0)) mask_scores(0, sc0);
     Probs p_cur;
     softmax(sc0, p_cur);   // m starts at -inf: nothing to rescale
@@ -453,7 +466,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // One block for the scheduler: P.V(j) and scores(j + 2) on the matrix
             // cores, softmax(j + 1) on the VALU.
             pv(j, p_cur);
-            const Scores sc2 = scores(j + 2);
+            Scores sc2;
+            scores(j + 2, sc2);
             rescale = softmax(sc1, p_next);
             // Interleave the block for the scheduler: one MFMA, then four VALU
             // instructions, for each MFMA of the block (left alone, the compiler
