@@ -208,10 +208,21 @@ def paged_workspace_size(B: int, H: int, Hkv: int, dtype, page_size: int, max_se
     return int(n.value)
 
 
-def _stream_handle(stream) -> int | None:
+def _stream_handle(stream, *owned) -> int | None:
+    """The HIP stream handle of ``stream`` (default: the current stream). ``owned`` are
+    tensors this call allocated (and the workspace zero-filled) on the current stream:
+    when the library runs on another stream, that stream first waits for the current
+    one, and the allocator keeps their memory until the other stream's work is done."""
+    cur = torch.cuda.current_stream()
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return cur.cuda_stream
+    s = stream if hasattr(stream, "cuda_stream") else torch.cuda.ExternalStream(int(stream))
+    owned = [t for t in owned if t is not None]
+    if owned and s.cuda_stream != cur.cuda_stream:
+        s.wait_stream(cur)
+        for t in owned:
+            t.record_stream(s)
+    return s.cuda_stream
 
 
 def _require(t: torch.Tensor, name: str, dtype=None) -> None:
@@ -257,14 +268,16 @@ def fd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor
               scale: float | None = None, ws: torch.Tensor | None = None, opt: FdOptions | None = None,
               stream=None) -> torch.Tensor:
     """Single decode over a contiguous cache: q [H, D], k/v [S, Hkv, D] -> o [H, D]."""
+    o_new = o is None
     H, Hkv, S, D, o = _single_args(q, k, v, o, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dt = _dtype_code(q.dtype)
     plan = decode_plan(H, Hkv, S, dt, 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    st = _stream_handle(stream, o if o_new else None, _keep if ws is None else None)
     _check(lib().fd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), H, Hkv, S, D, dt, float(scale),
-                           wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
+                           wp or None, wb, _opt_ptr(opt), st))
     return o
 
 
@@ -279,15 +292,16 @@ def fd_decode_fp8kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_scale: 
                     opt: FdOptions | None = None, stream=None) -> torch.Tensor:
     """Single decode over an FP8 E4M3 cache: K = k_scale * E4M3(k), V = v_scale * E4M3(v);
     q [H, D] f16/bf16, k/v [S, Hkv, D] codes -> o [H, D] in q's dtype."""
+    o_new = o is None
     H, Hkv, S, D, o = _single_args(q, k, v, o, _fp8_cache_dtype(k, "k"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dt = _fp8_code(q.dtype)
     plan = decode_plan(H, Hkv, S, dt, 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    st = _stream_handle(stream, o if o_new else None, _keep if ws is None else None)
     _check(lib().fd_decode_fp8kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), H, Hkv, S, D, dt,
-                                 float(scale), float(k_scale), float(v_scale), wp or None, wb, _opt_ptr(opt),
-                                 _stream_handle(stream)))
+                                 float(scale), float(k_scale), float(v_scale), wp or None, wb, _opt_ptr(opt), st))
     return o
 
 
@@ -323,6 +337,7 @@ def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     ``max_seq_len`` must bound every entry of ``seq_lens``; if omitted it is read
     from the device (a synchronising copy).
     """
+    o_new = o is None
     B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
         q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, q.dtype)
     if scale is None:
@@ -331,10 +346,11 @@ def fd_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     eff_max = min(max_seq_len, max_blocks * page_size)
     plan = paged_plan(B, H, Hkv, dt, page_size, eff_max, int(total_kv), 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    st = _stream_handle(stream, o if o_new else None, _keep if ws is None else None)
     _check(lib().fd_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                  seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
                                  num_pages, max_blocks, max_seq_len, int(total_kv), dt, wp or None, wb,
-                                 _opt_ptr(opt), _stream_handle(stream)))
+                                 _opt_ptr(opt), st))
     return o
 
 
@@ -344,14 +360,16 @@ def fd_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                             opt: FdOptions | None = None, stream=None) -> torch.Tensor:
     """``fd_paged_decode`` on the library's static per-GPU scratch (no workspace is
     allocated); calls that overlap on one GPU race on that scratch."""
+    o_new = o is None
     B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
         q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    st = _stream_handle(stream, o if o_new else None)
     _check(lib().fd_paged_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                          seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), B, H, Hkv, D,
                                          num_pages, max_blocks, max_seq_len, int(total_kv), _dtype_code(q.dtype),
-                                         _opt_ptr(opt), _stream_handle(stream)))
+                                         _opt_ptr(opt), st))
     return o
 
 
@@ -362,6 +380,7 @@ def fd_paged_decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           stream=None) -> torch.Tensor:
     """Batched paged GQA decode over FP8 E4M3 caches (codes as float8_e4m3fn or uint8)
     with per-tensor scales; otherwise as ``fd_paged_decode``."""
+    o_new = o is None
     B, H, Hkv, D, num_pages, page_size, max_blocks, max_seq_len, o = _paged_args(
         q, k_cache, v_cache, block_table, seq_lens, page_size, o, max_seq_len, _fp8_cache_dtype(k_cache, "k_cache"))
     if scale is None:
@@ -370,10 +389,11 @@ def fd_paged_decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     eff_max = min(max_seq_len, max_blocks * page_size)
     plan = paged_plan(B, H, Hkv, dt, page_size, eff_max, int(total_kv), 0, opt)
     wp, wb, _keep = _workspace(ws, plan["workspace_bytes"], q.device)
+    st = _stream_handle(stream, o if o_new else None, _keep if ws is None else None)
     _check(lib().fd_paged_decode_fp8kv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                        seq_lens.data_ptr(), page_size, o.data_ptr(), float(scale), float(k_scale),
                                        float(v_scale), B, H, Hkv, D, num_pages, max_blocks, max_seq_len,
-                                       int(total_kv), dt, wp or None, wb, _opt_ptr(opt), _stream_handle(stream)))
+                                       int(total_kv), dt, wp or None, wb, _opt_ptr(opt), st))
     return o
 
 
@@ -402,7 +422,8 @@ def fd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
         raise ValueError("k and v must both be [B, N, Hkv, D] with q's B, N and D")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, q.dtype)
-    if o is None:
+    o_new = o is None
+    if o_new:
         o = torch.empty_like(q)
     _require(o, "o", q.dtype)
     if o.shape != q.shape:
@@ -410,17 +431,17 @@ def fd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     Hkv = k.shape[2]
-    wp, wb = None, 0
+    wp, wb, ws_new = None, 0, None
     if ws is not False:
         need = prefill_workspace_size(B, N, Hkv, q.dtype)
         if need and ws is None:
-            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws = ws_new = torch.empty(need, dtype=torch.uint8, device=q.device)
         if isinstance(ws, torch.Tensor):
             _require(ws, "ws", torch.uint8)
             wp, wb = ws.data_ptr(), ws.numel()
+    st = _stream_handle(stream, o if o_new else None, ws_new)
     _check(lib().fd_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, N, H, Hkv, D,
-                            _dtype_code(q.dtype), float(scale), 1 if causal else 0, wp, wb, _opt_ptr(opt),
-                            _stream_handle(stream)))
+                            _dtype_code(q.dtype), float(scale), 1 if causal else 0, wp, wb, _opt_ptr(opt), st))
     return o
 
 
