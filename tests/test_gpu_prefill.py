@@ -280,3 +280,26 @@ def test_bf16_large_batch_many_chunks(device):
         ref, _ = oracle.decode_attention(d["q"][b, i, h:h + 1], d["k"][b, :i + 1, g:g + 1], d["v"][b, :i + 1, g:g + 1],
                                          d["scale"])
         assert_close(o[b, i, h:h + 1], ref, f"large batch b={b} row {i} head {h}")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_random_shapes(case, device):
+    """Twelve seeded draws of (B, N, H, Hkv, dtype, causal, scale): ragged N, GQA
+    from 1 to 8, both dtypes, both masks; bf16 through the workspace path, and
+    in cases 2, 6 and 10 also without it. Every output against the oracle."""
+    rng = np.random.default_rng(900 + case)
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 2, 3, 8]))
+    B = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 420))
+    dtype = ["bf16", "f16"][case % 2]
+    causal = bool(rng.integers(0, 2))
+    d = inputs.prefill_inputs(B, N, H, Hkv, 128, dtype, 910 + case)
+    scale = float(rng.choice([d["scale"], 0.3, -0.05]))
+    paths = [None, False] if dtype == "bf16" and case % 4 == 2 else [None]
+    ref, _ = oracle.prefill_attention(d["q"], d["k"], d["v"], scale, causal)
+    for ws in paths:
+        announce(f"seeded case {case}: B={B} N={N} H={H}/{Hkv} {dtype} causal={causal} scale={scale:.3f} ws={ws}")
+        o = fd.fd_prefill(d["q"].to(device), d["k"].to(device), d["v"].to(device), scale=scale, causal=causal, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(o.cpu(), ref, f"case {case}")
