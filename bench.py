@@ -371,7 +371,7 @@ def bench_prefill(args) -> dict:
     code = fd.binding.FD_DTYPE[q.dtype]
     stream = torch.cuda.current_stream()
     # bf16: the workspace of the f16-V path (the f16 copy of V and its flags), allocated once
-    ws_bytes = fd.prefill_workspace_size(w.B, w.N, w.Hkv, q.dtype)
+    ws_bytes = 0 if args.no_workspace else fd.prefill_workspace_size(w.B, w.N, w.Hkv, q.dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_ptr = ws.data_ptr() if ws_bytes else None
 
@@ -404,7 +404,8 @@ def bench_prefill(args) -> dict:
     ks = sorted(b.elapsed_time(e) / 1e3 for b, e in zip(begins, ends))
     k_mean = sum(ks) / len(ks)
     flops = w.flops()
-    traffic = load_traffic("prefill_kernel", w.name)
+    # the committed counters are those of the default path (for bf16, the f16-V kernel)
+    traffic = None if (args.no_workspace and w.dtype == "bf16") else load_traffic("prefill_kernel", w.name)
     line = {
         "metric": PREFILL_METRIC,
         "value": round(flops / step_s / 1e12, 2),
@@ -420,7 +421,8 @@ def bench_prefill(args) -> dict:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "Hkv": w.Hkv, "D": 128, "causal": w.causal,
                    "flops": flops, "parallelism": "single GPU",
-                   "pv": ("f16 MFMAs on an f16 copy of V (workspace)" if ws_bytes else "f16 MFMAs")},
+                   "pv": ("f16 MFMAs on an f16 copy of V (workspace)" if ws_bytes else
+                          "bf16 MFMAs, P split in two" if w.dtype == "bf16" else "f16 MFMAs")},
         "roofline": {"bound": "mfma", "achieved": round(flops / k_mean / 1e12, 2), "peak": PEAK_TFLOPS_16BIT,
                      "unit": "TFLOP/s", "frac": round(flops / k_mean / 1e12 / PEAK_TFLOPS_16BIT, 4),
                      "traffic": (round(traffic["bytes_per_launch"]) if traffic else None),
@@ -488,6 +490,8 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph (field \"graph\")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="prefill, bf16: pass no workspace (P.V on bf16 MFMAs with the split P)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
