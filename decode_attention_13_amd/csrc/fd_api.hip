@@ -413,6 +413,9 @@ fd_status run(const fd_plan &plan, fd_dtype dtype, bool paged, fd::SplitArgs &a,
         m.ws_lse = a.ws_lse;
         m.chunk = plan.chunk;
         m.num_splits = plan.num_splits;
+        // Contiguous grid (slices, splits): workgroup (x, y) is dispatched to XCD
+        // (y * slices + x) mod 8 = x mod 8 when slices is a multiple of 8.
+        m.xcd_group = (!paged && plan.grid_x % 8 == 0 && m.H % 8 == 0 && plan.grid_z == 1) ? m.H / plan.grid_x : 0;
         e = fd::launch_merge(fd::query_dtype(dtype), paged, B, m, stream);
         if (e != hipSuccess) return fail(FD_ERR_LAUNCH, "merge kernel launch: %s", hipGetErrorString(e));
     }

@@ -89,6 +89,10 @@ struct MergeArgs {
     int max_len;              // contiguous: S; paged: clamp bound for seq_lens
     int chunk;
     int num_splits;
+    // > 0: head h of the split grid's slice h / xcd_group ran on XCD (slice mod 8);
+    // workgroup i of the merge takes a head of slice = i mod 8 (mod 8), so it reads
+    // partials its XCD's L2 may still hold. 0: workgroup i takes head i.
+    int xcd_group;
 };
 
 struct LaunchShape {

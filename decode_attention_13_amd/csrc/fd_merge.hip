@@ -75,7 +75,11 @@ __device__ __forceinline__ void merge_span(const float *ws_o_row, const float *l
 // rescaled to the common max.
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
-    const int h = blockIdx.x;
+    int h = blockIdx.x;
+    if (a.xcd_group > 0) {  // a bijection of [0, H): workgroup i on XCD i mod 8 takes a head split there
+        const int c = h & 7, k = h >> 3;
+        h = (c + 8 * (k / a.xcd_group)) * a.xcd_group + k % a.xcd_group;
+    }
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
